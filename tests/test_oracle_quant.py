@@ -1,0 +1,188 @@
+"""Pins of the oracle's quantisers (no GPU).
+
+What pins them, besides themselves:
+  * hand-worked tie cases (golden/quant_ties.json) fix the rounding mode and
+    the scale definition;
+  * exact rational arithmetic (fractions) fixes the correctly rounded fp32
+    divisions of the scale and of the quotient;
+  * the quantise/dequantise round-trip bound |x - q s| <= s/2 (1 + 2^-16);
+  * identities between the schemes (token == group when K == 128; the
+    channel-wise weight quantiser is the token quantiser on W);
+  * the FP8 -> BF16 -> INT8 conversion is exactly equivariant to power-of-two
+    scale_inv, and with scale_inv = 1 its bf16 step is exact.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats, quant
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _round_to_f32(fr):
+    """Round a Fraction to the nearest float32, ties to even (exact search)."""
+    f = np.float32(float(fr))            # within an ulp or so of the answer
+    cands = [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                     int(np.array(c, np.float32).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def _bf16_tensor_bits(x):
+    return synth.to_numpy(x)
+
+
+def test_golden_ties():
+    with open(os.path.join(HERE, "golden", "quant_ties.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        vals = np.zeros(case["pad_to"], np.float32)
+        vals[: len(case["values"])] = case["values"]
+        bits = formats.f32_to_bf16_bits(vals)
+        assert np.array_equal(formats.bf16_bits_to_f32(bits), vals)     # exact in bf16
+        for fn in (quant.quant_act_group, quant.quant_act_token):
+            q, s = fn(bits[None, :])
+            assert np.float32(s.reshape(-1)[0]) == np.float32(case["scale"]), case["name"]
+            assert q[0, : len(case["q"])].tolist() == case["q"], case["name"]
+            assert np.all(q[0, len(case["q"]):] == 0)
+
+
+def test_scale_and_quotient_are_correctly_rounded_fp32_divisions():
+    rng = np.random.default_rng(1)
+    x = synth.to_numpy(synth.activations(4, 1024, seed=7, outlier_frac=0.01, outlier_factor=20.0))
+    q, s = quant.quant_act_group(x)
+    x32 = formats.bf16_bits_to_f32(x)
+    g = x32.reshape(4, 8, 128)
+    for (m, kb) in [(0, 0), (1, 3), (2, 7), (3, 5)]:
+        amax = Fraction(float(np.abs(g[m, kb]).max()))
+        s_exact = _round_to_f32(amax / 127)
+        assert s[m, kb] == s_exact
+        for j in rng.integers(0, 128, 24):
+            quo = _round_to_f32(Fraction(float(g[m, kb, j])) / Fraction(float(s_exact)))
+            want = int(np.rint(np.float64(quo)))
+            assert q[m, kb * 128 + j] == max(-127, min(127, want))
+
+
+def test_round_trip_bound_and_amax_maps_to_127():
+    x = synth.to_numpy(synth.activations(64, 2048, seed=3))
+    x32 = formats.bf16_bits_to_f32(x).astype(np.float64)
+    for fn, shape in ((quant.quant_act_group, (64, 16)), (quant.quant_act_token, (64,))):
+        q, s = fn(x)
+        assert s.shape == shape and q.dtype == np.int8
+        assert q.min() >= -127 and q.max() <= 127
+        se = np.repeat(s, 128, axis=1) if s.ndim == 2 else s[:, None]
+        err = np.abs(x32 - q.astype(np.float64) * se.astype(np.float64))
+        assert np.all(err <= se * 0.5 * (1 + 2.0 ** -16))
+        # the element of largest magnitude of each group lands on +-127
+        if s.ndim == 2:
+            g = x32.reshape(64, 16, 128)
+            idx = np.abs(g).argmax(axis=2)
+            qq = q.reshape(64, 16, 128)
+            picked = np.take_along_axis(qq, idx[:, :, None], axis=2)[..., 0]
+        else:
+            idx = np.abs(x32).argmax(axis=1)
+            picked = q[np.arange(64), idx]
+        assert np.all(np.abs(picked.astype(int)) == 127)
+
+
+def test_zero_group_gives_zero_codes_and_eps_scale():
+    x = np.zeros((2, 256), np.uint16)
+    x[1, 128:] = formats.f32_to_bf16_bits(np.full(128, 0.5, np.float32))
+    q, s = quant.quant_act_group(x)
+    eps_scale = _round_to_f32(Fraction(float(np.float32(1e-10))) / 127)
+    assert s[0, 0] == eps_scale and s[0, 1] == eps_scale and s[1, 0] == eps_scale
+    assert np.all(q[0] == 0) and np.all(q[1, :128] == 0) and np.all(q[1, 128:] == 127)
+
+
+def test_group_equals_token_when_k_is_one_block():
+    x = synth.to_numpy(synth.activations(32, 128, seed=5))
+    qg, sg = quant.quant_act_group(x)
+    qt, st = quant.quant_act_token(x)
+    assert np.array_equal(qg, qt) and np.array_equal(sg[:, 0], st)
+
+
+def test_tile_quantiser_against_groupwise_definition():
+    """A 128x128 tile is one quantisation group: quantising the flattened tile
+    as one token row must give the same codes and scale."""
+    w = synth.to_numpy(synth.weights(200, 384, seed=9))            # ragged last tile (72 rows)
+    q, s = quant.quant_weight_block(w)
+    assert s.shape == (2, 3)
+    for nb in range(2):
+        r0, r1 = nb * 128, min(200, nb * 128 + 128)
+        for kb in range(3):
+            tile = w[r0:r1, kb * 128:(kb + 1) * 128]
+            qt, st = quant.quant_act_token(tile.reshape(1, -1))
+            assert st[0] == s[nb, kb]
+            assert np.array_equal(qt.reshape(tile.shape), q[r0:r1, kb * 128:(kb + 1) * 128])
+
+
+def test_requant_power_of_two_equivariance():
+    codes, _ = synth.fp8_weights(192, 256, seed=11)
+    codes = codes.numpy()
+    base = np.full((2, 2), 1.0, np.float32)
+    q0, s0, w0 = quant.requant_fp8_to_int8_block(codes, base)
+    # scale_inv = 1: every E4M3 value is exact in bf16, so the bf16 step is exact
+    assert np.array_equal(formats.bf16_bits_to_f32(w0), formats.e4m3fn_to_f32(codes))
+    for e in (-20, -7, 3, 9):
+        q1, s1, _ = quant.requant_fp8_to_int8_block(codes, base * np.float32(2.0 ** e))
+        assert np.array_equal(q1, q0)
+        assert np.array_equal(s1, (s0 * np.float32(2.0 ** e)).astype(np.float32))
+
+
+def test_requant_uses_each_tiles_scale_inv():
+    """A tile-wise scale_inv that differs per tile must act only on its tile:
+    with per-tile powers of two, each tile's codes match the unit-scale codes
+    and its scale is multiplied by that tile's power of two."""
+    codes, _ = synth.fp8_weights(256, 384, seed=12)
+    codes = codes.numpy()
+    exps = np.array([[-3, 0, 5], [7, -9, 2]])
+    si = (2.0 ** exps).astype(np.float32)
+    q0, s0, _ = quant.requant_fp8_to_int8_block(codes, np.ones((2, 3), np.float32))
+    q1, s1, _ = quant.requant_fp8_to_int8_block(codes, si)
+    assert np.array_equal(q0, q1)
+    assert np.array_equal(s1, (s0 * si).astype(np.float32))
+
+
+def test_requant_matches_library_cast_route():
+    """FP8 -> BF16 via torch's own casts (fp8 -> fp32, multiply, -> bf16) then
+    tile quantisation gives the same result as the oracle's requant."""
+    codes, si = synth.fp8_weights(200, 256, seed=13)
+    f = codes.view(torch.float8_e4m3fn).to(torch.float32)
+    rows = torch.arange(200) // 128
+    cols = torch.arange(256) // 128
+    wb = (f * si[rows][:, cols]).to(torch.bfloat16)
+    q_ref, s_ref = quant.quant_weight_block(synth.to_numpy(wb))
+    q, s, wbits = quant.requant_fp8_to_int8_block(codes.numpy(), si.numpy())
+    assert np.array_equal(wbits, synth.to_numpy(wb))
+    assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
+
+
+def test_channel_wise_is_more_exposed_to_outliers():
+    """Page 1 section 2.3: per-channel/per-token groups meet outliers more often
+    than small groups, so their quantisation error is larger.  Statistical
+    property on the outlier-laden activations (not a parity check)."""
+    x = synth.to_numpy(synth.activations(64, 7168, seed=1))
+    x32 = formats.bf16_bits_to_f32(x).astype(np.float64)
+    qg, sg = quant.quant_act_group(x)
+    qt, st = quant.quant_act_token(x)
+    eg = np.abs(x32 - qg * np.repeat(sg, 128, axis=1)).mean()
+    et = np.abs(x32 - qt * st[:, None]).mean()
+    assert et > 2 * eg
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fp16_and_bf16_inputs_give_the_same_codes_for_common_values(dtype):
+    # values exactly representable in both formats quantise identically
+    rng = np.random.default_rng(2)
+    v = (rng.integers(-255, 256, (4, 256)) / 64.0).astype(np.float32)
+    x = v.astype(np.float16) if dtype == "fp16" else formats.f32_to_bf16_bits(v)
+    q, s = quant.quant_act_group(x)
+    q2, s2 = quant.quant_act_group(v)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
