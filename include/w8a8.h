@@ -1,0 +1,189 @@
+/*
+ * w8a8.h - C ABI of libw8a8.so: W8A8 INT8 linear layers (block-wise and
+ * channel-wise schemes) on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the page "DeepSeek R1 INT8 quantisation
+ * in SGLang" (Meituan team article), section 2.3 "Quantisation method
+ * design", with the symmetric INT8 quantiser of the page "FP8 vs INT8
+ * quantisation for DeepSeek", section 3.2.1 (int8 branch):
+ *
+ *   scale = max(amax, 1e-10f) / 127           fp32 IEEE division
+ *   q     = clamp(round_half_even(x / scale), -127, 127)   x / scale in fp32
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls; calls are
+ *     thread-safe.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream) and returns without synchronising.
+ *     Results are visible once the stream reaches that point.
+ *   - Layouts are row-major and contiguous.  Activations are A[M][K],
+ *     weights W[N][K] (nn.Linear layout), outputs Y[M][N] = A . W^T.
+ *   - K must be a multiple of 128 (the K block / group size); KB = K / 128,
+ *     NB = ceil(N / 128).  M == 0 (or N == 0) is a valid no-op.
+ *   - Data pointers (int8, bf16, fp16, fp8, outputs) must be 16-byte aligned;
+ *     scale pointers 4-byte aligned.  Outputs must not alias inputs.
+ *   - int8 codes are always in [-127, 127]; scales are fp32.
+ *   - bf16 and fp16 values are passed as their 16-bit patterns.
+ *   - Inputs are finite.  NaN or infinite inputs (and the FP8 NaN codes
+ *     0x7F / 0xFF) give unspecified results but never out-of-bounds access.
+ *   - Results are deterministic: no floating-point atomics; rerunning a call
+ *     on the same inputs gives the same bits.
+ *   - Return 0 (W8_OK) on success, otherwise a negative w8_status; nothing is
+ *     enqueued when an argument check fails.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum w8_status {
+  W8_OK = 0,
+  W8_ERR_NULL = -1,   /* a required pointer is NULL */
+  W8_ERR_SHAPE = -2,  /* negative size, K % 128 != 0, or a size beyond the limits below */
+  W8_ERR_ALIGN = -3,  /* a pointer is not aligned as required */
+  W8_ERR_DTYPE = -4,  /* unsupported dtype code */
+  W8_ERR_LAUNCH = -5  /* the HIP runtime rejected a kernel launch */
+};
+
+enum w8_dtype { W8_BF16 = 0, W8_FP16 = 1, W8_FP32 = 2, W8_I32 = 3 };
+
+/* Size limits: M, N <= 2^31 - 1 and K <= 2^20, so that every index fits the
+   kernels' 32-bit row arithmetic; M * K and N * K < 2^40. */
+
+/* Version of this ABI (bumped on any signature change). */
+int w8_abi_version(void);
+
+/* Human-readable text of a w8_status code (static storage). */
+const char* w8_status_string(int status);
+
+/*
+ * Online per-token-group activation quantisation (block-wise scheme; page 1
+ * section 2.3: "each token's vector is split into groups, quantised group by
+ * group").  Group = 1 x 128 along K, aligned with the 128-wide weight blocks.
+ *   x      [M][K]  bf16 (x_dtype = W8_BF16) or fp16 (W8_FP16) bit patterns
+ *   q      [M][K]  int8 out
+ *   scale  [M][KB] fp32 out, scale[m][kb] for elements k in [128 kb, 128 kb + 128)
+ * With x = W[N][K] in fp16 this is also the group-wise weight quantiser of
+ * the W8A16 variant (page 5, symmetric group-wise INT8 weights).
+ */
+int quant_act_group(const void* x, int x_dtype, int64_t M, int64_t K,
+                    int8_t* q, float* scale, void* stream);
+
+/*
+ * Online per-token activation quantisation (channel-wise scheme; page 1
+ * section 2.3: activations quantised online token by token).  One scale per
+ * row over the whole K.  K <= 2^20.
+ *   x [M][K] bf16/fp16 -> q [M][K] int8, scale [M] fp32.
+ * With x = W[N][K] this is the channel-wise weight quantiser (one scale per
+ * output channel: "each column of the weight is one group" in X.W notation).
+ */
+int quant_act_token(const void* x, int x_dtype, int64_t M, int64_t K,
+                    int8_t* q, float* scale, void* stream);
+
+/*
+ * Block-wise weight quantisation of bf16 weights in 128 x 128 tiles (page 1
+ * section 2.3, block-wise paragraph).  The last tile row may hold fewer than
+ * 128 rows; its amax covers the rows that exist.
+ *   w [N][K] bf16 -> w_q [N][K] int8, w_scale [NB][KB] fp32.
+ */
+int quant_weight_block(const void* w, int64_t N, int64_t K,
+                       int8_t* w_q, float* w_scale, void* stream);
+
+/*
+ * Offline weight conversion of page 1 section 2.3: the FP8 checkpoint is
+ * dequantised to BF16, then requantised to INT8 in 128 x 128 tiles.
+ *   w_fp8     [N][K]  OCP FP8-E4M3FN codes (bias 7, max 448, S.1111.111 NaN)
+ *   scale_inv [NB][KB] fp32: dequantised value = fp8 value * scale_inv
+ *   w_q [N][K] int8, w_scale [NB][KB] fp32 out
+ *   w_bf16_or_null [N][K] bf16 out (the intermediate) or NULL to skip it
+ * BF16 step: bf16_round_nearest_even(fp32(fp8 * scale_inv[n/128][k/128])).
+ */
+int requant_fp8_to_int8_block(const uint8_t* w_fp8, const float* scale_inv,
+                              int64_t N, int64_t K, int8_t* w_q, float* w_scale,
+                              uint16_t* w_bf16_or_null, void* stream);
+
+/*
+ * Channel-wise counterpart of the offline conversion (page 1 section 2.3,
+ * channel-wise paragraph): FP8 -> BF16 as above, then one scale per output
+ * channel (row of W).  w_scale [N] fp32.  K <= 2^20.
+ */
+int requant_fp8_to_int8_channel(const uint8_t* w_fp8, const float* scale_inv,
+                                int64_t N, int64_t K, int8_t* w_q, float* w_scale,
+                                void* stream);
+
+/*
+ * Block-wise W8A8 GEMM (page 1 section 2.3, block-wise paragraph and its
+ * Figure 3): int32 partial sums per 128-wide K block, dequantised in fp32
+ * inside the K loop:
+ *   Y[m][n] = sum_kb a_scale[m][kb] * w_scale[n/128][kb] * P[kb][m][n],
+ *   P[kb][m][n] = sum_{k in block kb} A[m][k] * W[n][k]   (exact int32).
+ *   A [M][K] int8, a_scale [M][KB], W [N][K] int8, w_scale [NB][KB]
+ *   Y [M][N] bf16 (y_dtype W8_BF16) or fp32 (W8_FP32).
+ * The bf16 output is the round-to-nearest-even of the fp32 result.
+ */
+int gemm_w8a8_block(const int8_t* A, const float* a_scale,
+                    const int8_t* W, const float* w_scale,
+                    void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                    void* stream);
+
+/*
+ * Channel-wise W8A8 GEMM (page 1 section 2.3, channel-wise paragraph): one
+ * dequantisation after the INT8 matmul:
+ *   ACC[m][n] = sum_k A[m][k] * W[n][k]   (exact int32; K <= 2^17 keeps it
+ *                                          inside int32 for codes in +-127)
+ *   Y[m][n]   = fp32(fp32(ACC) * fp32(a_scale[m] * w_scale[n]))
+ *   A [M][K] int8, a_scale [M], W [N][K] int8, w_scale [N]
+ *   Y [M][N] bf16, fp32, or int32 (y_dtype W8_I32: raw ACC, scales unused and
+ *   may be NULL).
+ */
+int gemm_w8a8_channel(const int8_t* A, const float* a_scale,
+                      const int8_t* W, const float* w_scale,
+                      void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                      void* stream);
+
+/*
+ * The int32 block partial sums of the block-wise GEMM, for bit-exact checks:
+ *   P [KB][M][N] int32, P[kb][m][n] as defined for gemm_w8a8_block.
+ */
+int gemm_w8a8_block_partials(const int8_t* A, const int8_t* W, int32_t* P,
+                             int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * W8A16 group-wise GEMM (page 5, "DeepSeek-R1-0528-Qwen3-8B Int8 W8A16"
+ * release note: symmetric group-wise INT8 weights, fp16 activations), groups
+ * of 128 along K:
+ *   Y[m][n] = sum_g w_scale[n][g] * sum_{k in group g} x[m][k] * W[n][k]
+ *   x [M][K] fp16, W [N][K] int8, w_scale [N][KB] fp32, Y [M][N] fp16.
+ * Each x * W product is exact in fp32; sums are fp32.
+ */
+int gemm_w8a16_group(const uint16_t* x, const int8_t* W, const float* w_scale,
+                     uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Grouped block-wise W8A8 GEMM for mixture-of-experts layers (DeepSeek is an
+ * MoE model, page 4 section 1.2).  Rows expert_offsets[e] .. expert_offsets[e+1]-1
+ * of the expert-sorted activations are multiplied by expert e's weights with
+ * the block-wise formula of gemm_w8a8_block.
+ *   A [P][K] int8, a_scale [P][KB], W [E][N][K] int8, w_scale [E][NB][KB]
+ *   expert_offsets [E+1] int32 DEVICE array, non-decreasing, offsets[0] = 0,
+ *   offsets[E] <= P (rows past offsets[E] are left untouched).
+ *   Y [P][N] bf16 or fp32.  E <= 4096.
+ * The offsets are read on the device only; offsets that break the contract
+ * give unspecified output rows but no out-of-bounds access.
+ */
+int gemm_w8a8_block_grouped(const int8_t* A, const float* a_scale,
+                            const int8_t* W, const float* w_scale,
+                            const int32_t* expert_offsets, void* Y, int y_dtype,
+                            int64_t E, int64_t P, int64_t N, int64_t K,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,162 @@
+"""GPU parity of the GEMM kernels against the CPU oracle.
+
+Bars (same seeded inputs on both sides):
+  * int32 block partials P and the channel-wise raw accumulator: bit-exact;
+  * channel-wise fp32 output: bit-exact with the oracle's fp32 path (the kernel
+    evaluates fp32(fp32(ACC) * fp32(sa * sw)) exactly as the oracle does);
+  * block-wise / W8A16 / grouped fp32 outputs: normwise relative error
+    <= 1e-3 against the oracle's fp32 path and <= 1e-2 against its fp64 path;
+  * bf16 outputs: the round-to-nearest-even of the same kernel's fp32 output
+    (and <= 1e-2 against fp64).
+Shapes cover several tiles plus ragged tails in M, N (576 = 4.5 N blocks) and
+the decode (M <= 64) and tile (M > 64) code paths.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import w8a8_int8_quantized_amd as w8
+from oracle import formats, gemm, quant, routing
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL32, TOL64 = 1e-3, 1e-2
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _bf16_of(y32_gpu):
+    return formats.f32_to_bf16_bits(_np(y32_gpu))
+
+
+def _inputs(M, N, K, seed, scheme):
+    x = synth.activations(M, K, seed=seed)
+    w = synth.weights(N, K, seed=seed + 1)
+    xn, wn = synth.to_numpy(x), synth.to_numpy(w)
+    if scheme == "block":
+        qa, sa = quant.quant_act_group(xn)
+        qw, sw = quant.quant_weight_block(wn)
+    else:
+        qa, sa = quant.quant_act_token(xn)
+        qw, sw = quant.quant_act_token(wn)
+    return qa, sa, qw, sw
+
+
+def _dev(*arrs):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrs]
+
+
+SHAPES = [(1, 256, 256), (8, 576, 1024), (16, 256, 256), (32, 1000, 512), (64, 576, 768),
+          (65, 256, 256), (128, 512, 1024), (300, 576, 512), (513, 384, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_channel_gemm_bit_exact(M, N, K):
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M * 7 + N, scheme="channel")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    ACC, y64, y32 = gemm.gemm_channel(qa, sa, qw, sw)
+    acc = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)
+    assert np.array_equal(_np(acc), ACC)
+    yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
+    assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
+    yb = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+    assert gemm.normwise_rel_err(_np(yb.float()), y64) <= TOL64
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 256, 256), (300, 576, 512), (129, 640, 1024)])
+def test_block_partials_bit_exact(M, N, K):
+    qa, _, qw, _ = _inputs(M, N, K, seed=M + 3, scheme="block")
+    A, W = _dev(qa, qw)
+    P = w8.gemm_w8a8_block_partials(A, W)
+    assert np.array_equal(_np(P), gemm.block_partials(qa, qw))
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_block_gemm(M, N, K):
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M * 5 + K, scheme="block")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    _, y64, y32 = gemm.gemm_block(qa, sa, qw, sw)
+    yf = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    e32 = gemm.normwise_rel_err(_np(yf), y32)
+    e64 = gemm.normwise_rel_err(_np(yf), y64)
+    assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+    assert e32 <= 1e-5          # in practice the fp32 orders differ by a few ulps
+    yb = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+    assert gemm.normwise_rel_err(_np(yb.float()), y64) <= TOL64
+
+
+def test_block_equals_channel_when_k_is_one_block():
+    M, N, K = 70, 256, 128
+    qa, sa, qw, sw = _inputs(M, N, K, seed=1, scheme="block")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    sw_ch = torch.from_numpy(sw[np.arange(N) // 128, 0].copy()).to(DEV)
+    yb = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    yc = w8.gemm_w8a8_channel(A, SA.reshape(-1).contiguous(), W, sw_ch, out_dtype=torch.float32)
+    _, _, yb32 = gemm.gemm_block(qa, sa, qw, sw)
+    assert gemm.normwise_rel_err(_np(yb), yb32) <= 1e-6
+    assert gemm.normwise_rel_err(_np(yc), yb32) <= 1e-6
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (8, 1000, 4096), (32, 512, 1024), (64, 384, 12288), (100, 256, 256)])
+def test_w8a16_group(M, N, K):
+    x = synth.activations(M, K, seed=M, dtype=torch.float16)
+    w = synth.weights(N, K, seed=N, dtype=torch.float16)
+    qw, sw = quant.quant_act_group(w.numpy())
+    y64, y32 = gemm.gemm_w8a16_group(x.numpy(), qw, sw)
+    X, W, SW = _dev(x.numpy(), qw, sw)
+    y = w8.gemm_w8a16_group(X, W, SW)
+    yn = _np(y).astype(np.float32)
+    e32, e64 = gemm.normwise_rel_err(yn, y32), gemm.normwise_rel_err(yn, y64)
+    assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+
+
+def test_grouped_moe_gemm_with_empty_experts():
+    E, T, topk, K, N = 12, 200, 2, 512, 384
+    lg = synth.router_logits(T, E, seed=4).numpy()
+    lg[:, 5] = -100.0                                 # expert 5 gets no tokens
+    lg[:, 7] = -100.0
+    rows, exps, offs = routing.topk_route(lg, topk)
+    assert offs[6] == offs[5] and offs[8] == offs[7]
+    x = synth.to_numpy(synth.activations(T, K, seed=8))
+    qa, sa = quant.quant_act_group(x[rows])
+    qw = np.empty((E, N, K), np.int8)
+    sw = np.empty((E, 3, K // 128), np.float32)
+    for e in range(E):
+        qw[e], sw[e] = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=100 + e)))
+    y64, y32 = gemm.gemm_block_grouped(qa, sa, qw, sw, offs)
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    OFF = torch.from_numpy(offs.astype(np.int32)).to(DEV)
+    y = w8.gemm_w8a8_block_grouped(A, SA, W, SW, OFF, out_dtype=torch.float32)
+    yn = _np(y)
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        if r1 > r0:
+            assert gemm.normwise_rel_err(yn[r0:r1], y32[r0:r1]) <= TOL32
+            assert gemm.normwise_rel_err(yn[r0:r1], y64[r0:r1]) <= TOL64
+    yb = w8.gemm_w8a8_block_grouped(A, SA, W, SW, OFF, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(y))
+
+
+def test_gemms_are_deterministic():
+    qa, sa, qw, sw = _inputs(300, 576, 1024, seed=2, scheme="block")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    a = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    b = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    assert torch.equal(a, b)
+    a = w8.gemm_w8a8_block(A[:8].contiguous(), SA[:8].contiguous(), W, SW, out_dtype=torch.float32)
+    b = w8.gemm_w8a8_block(A[:8].contiguous(), SA[:8].contiguous(), W, SW, out_dtype=torch.float32)
+    assert torch.equal(a, b)
+
+
+def test_empty_gemms_are_noops():
+    A = torch.empty(0, 256, dtype=torch.int8, device=DEV)
+    SA = torch.empty(0, 2, dtype=torch.float32, device=DEV)
+    W = torch.zeros(128, 256, dtype=torch.int8, device=DEV)
+    SW = torch.ones(1, 2, dtype=torch.float32, device=DEV)
+    assert w8.gemm_w8a8_block(A, SA, W, SW).shape == (0, 128)

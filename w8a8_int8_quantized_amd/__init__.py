@@ -1,0 +1,234 @@
+"""MI355X (gfx950) W8A8 INT8 linear layers: thin Python binding of libw8a8.so.
+
+Every function here only checks tensors, allocates outputs with torch (device
+memory only) and calls the C ABI declared in include/w8a8.h on torch's current
+HIP stream.  All arithmetic runs in the library's HIP kernels; there is no
+fallback: if libw8a8.so is missing, importing this package raises.
+
+    q, s  = quant_act_group(x)                 # block-wise activations, 1x128 groups
+    q, s  = quant_act_token(x)                 # channel-wise activations, one scale per row
+    wq, ws = quant_weight_block(w_bf16)        # 128x128 weight tiles
+    wq, ws = requant_fp8_to_int8_block(w_fp8, scale_inv)
+    y = gemm_w8a8_block(q, s, wq, ws)          # bf16 (or fp32) output
+    y = gemm_w8a8_channel(q, s, wq, ws)
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw8a8.so")
+
+W8_BF16, W8_FP16, W8_FP32, W8_I32 = 0, 1, 2, 3
+GROUP = 128
+
+_FUNCS = {
+    "w8_abi_version": (ctypes.c_int, []),
+    "w8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "quant_act_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "quant_act_token": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "quant_weight_block": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "requant_fp8_to_int8_block": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]),
+    "requant_fp8_to_int8_channel": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_void_p]),
+    "gemm_w8a8_block": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p]),
+    "gemm_w8a8_channel": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_void_p]),
+    "gemm_w8a8_block_partials": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "gemm_w8a16_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "gemm_w8a8_block_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_void_p]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python w8a8_int8_quantized_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _FUNCS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class W8Error(RuntimeError):
+    pass
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise W8Error(f"{what}: {lib.w8_status_string(rc).decode()} (status {rc})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise W8Error("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise W8Error("tensors must be contiguous")
+
+
+def _act_dtype(x):
+    if x.dtype == torch.bfloat16:
+        return W8_BF16
+    if x.dtype == torch.float16:
+        return W8_FP16
+    raise W8Error(f"activations must be bf16 or fp16, got {x.dtype}")
+
+
+def _out_code(dt):
+    return {torch.bfloat16: W8_BF16, torch.float32: W8_FP32, torch.int32: W8_I32}[dt]
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ----------------------------------------------------------------- quantisers
+def quant_act_group(x, out=None):
+    """Per-token-group (1x128) quantisation of x [M, K] (bf16 or fp16)."""
+    _dev(x)
+    M, K = x.shape
+    q, s = out if out is not None else (_empty((M, K), torch.int8, x), _empty((M, K // GROUP), torch.float32, x))
+    _check(lib.quant_act_group(_p(x), _act_dtype(x), M, K, _p(q), _p(s), _stream()), "quant_act_group")
+    return q, s
+
+
+def quant_act_token(x, out=None):
+    """Per-token quantisation of x [M, K] (bf16 or fp16): one scale per row."""
+    _dev(x)
+    M, K = x.shape
+    q, s = out if out is not None else (_empty((M, K), torch.int8, x), _empty((M,), torch.float32, x))
+    _check(lib.quant_act_token(_p(x), _act_dtype(x), M, K, _p(q), _p(s), _stream()), "quant_act_token")
+    return q, s
+
+
+def quant_weight_block(w, out=None):
+    """128x128 tile quantisation of bf16 weights w [N, K]."""
+    _dev(w)
+    if w.dtype != torch.bfloat16:
+        raise W8Error("quant_weight_block takes bf16 weights")
+    N, K = w.shape
+    NB = (N + GROUP - 1) // GROUP
+    q, s = out if out is not None else (_empty((N, K), torch.int8, w), _empty((NB, K // GROUP), torch.float32, w))
+    _check(lib.quant_weight_block(_p(w), N, K, _p(q), _p(s), _stream()), "quant_weight_block")
+    return q, s
+
+
+def quant_weight_channel(w):
+    """Channel-wise weight quantisation: one scale per output channel (row)."""
+    return quant_act_token(w)
+
+
+def requant_fp8_to_int8_block(w_fp8, scale_inv, return_bf16=False):
+    """FP8-E4M3FN codes [N, K] (uint8) with scale_inv [NB, KB] -> BF16 -> INT8 128x128 tiles."""
+    _dev(w_fp8, scale_inv)
+    if w_fp8.dtype == torch.float8_e4m3fn:
+        w_fp8 = w_fp8.view(torch.uint8)
+    N, K = w_fp8.shape
+    NB = (N + GROUP - 1) // GROUP
+    q = _empty((N, K), torch.int8, w_fp8)
+    s = _empty((NB, K // GROUP), torch.float32, w_fp8)
+    wb = _empty((N, K), torch.bfloat16, w_fp8) if return_bf16 else None
+    _check(lib.requant_fp8_to_int8_block(_p(w_fp8), _p(scale_inv), N, K, _p(q), _p(s), _p(wb), _stream()),
+           "requant_fp8_to_int8_block")
+    return (q, s, wb) if return_bf16 else (q, s)
+
+
+def requant_fp8_to_int8_channel(w_fp8, scale_inv):
+    """FP8-E4M3FN codes [N, K] with scale_inv [NB, KB] -> BF16 -> per-channel INT8."""
+    _dev(w_fp8, scale_inv)
+    if w_fp8.dtype == torch.float8_e4m3fn:
+        w_fp8 = w_fp8.view(torch.uint8)
+    N, K = w_fp8.shape
+    q = _empty((N, K), torch.int8, w_fp8)
+    s = _empty((N,), torch.float32, w_fp8)
+    _check(lib.requant_fp8_to_int8_channel(_p(w_fp8), _p(scale_inv), N, K, _p(q), _p(s), _stream()),
+           "requant_fp8_to_int8_channel")
+    return q, s
+
+
+# ---------------------------------------------------------------------- GEMMs
+def gemm_w8a8_block(A, a_scale, W, w_scale, out_dtype=torch.bfloat16, out=None):
+    """Block-wise W8A8 GEMM: Y[M, N] = sum_kb sa[m,kb] sw[n/128,kb] P[kb,m,n]."""
+    _dev(A, a_scale, W, w_scale)
+    M, K = A.shape
+    N = W.shape[0]
+    y = out if out is not None else _empty((M, N), out_dtype, A)
+    _check(lib.gemm_w8a8_block(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(y), _out_code(y.dtype), M, N, K,
+                               _stream()), "gemm_w8a8_block")
+    return y
+
+
+def gemm_w8a8_channel(A, a_scale, W, w_scale, out_dtype=torch.bfloat16, out=None):
+    """Channel-wise W8A8 GEMM: Y = (A . W^T) * sa[m] * sw[n]; int32 output = raw accumulator."""
+    _dev(A, W, a_scale, w_scale)
+    M, K = A.shape
+    N = W.shape[0]
+    y = out if out is not None else _empty((M, N), out_dtype, A)
+    _check(lib.gemm_w8a8_channel(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(y), _out_code(y.dtype), M, N, K,
+                                 _stream()), "gemm_w8a8_channel")
+    return y
+
+
+def gemm_w8a8_block_partials(A, W):
+    """The exact int32 partial sums P[kb, m, n] of the block-wise GEMM."""
+    _dev(A, W)
+    M, K = A.shape
+    N = W.shape[0]
+    P = _empty((K // GROUP, M, N), torch.int32, A)
+    _check(lib.gemm_w8a8_block_partials(_p(A), _p(W), _p(P), M, N, K, _stream()), "gemm_w8a8_block_partials")
+    return P
+
+
+def gemm_w8a16_group(x, W, w_scale, out=None):
+    """W8A16: fp16 x [M, K], int8 W [N, K], group scales [N, K/128] -> fp16 Y [M, N]."""
+    _dev(x, W, w_scale)
+    if x.dtype != torch.float16:
+        raise W8Error("gemm_w8a16_group takes fp16 activations")
+    M, K = x.shape
+    N = W.shape[0]
+    y = out if out is not None else _empty((M, N), torch.float16, x)
+    _check(lib.gemm_w8a16_group(_p(x), _p(W), _p(w_scale), _p(y), M, N, K, _stream()), "gemm_w8a16_group")
+    return y
+
+
+def gemm_w8a8_block_grouped(A, a_scale, W, w_scale, expert_offsets, out_dtype=torch.bfloat16, out=None):
+    """Grouped block-wise GEMM over expert-sorted rows; W [E, N, K], offsets int32 [E+1] on the GPU."""
+    _dev(A, a_scale, W, w_scale, expert_offsets)
+    if expert_offsets.dtype != torch.int32:
+        raise W8Error("expert_offsets must be int32")
+    P, K = A.shape
+    E, N, _ = W.shape
+    y = out if out is not None else _empty((P, N), out_dtype, A)
+    _check(lib.gemm_w8a8_block_grouped(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(expert_offsets), _p(y),
+                                       _out_code(y.dtype), E, P, N, K, _stream()), "gemm_w8a8_block_grouped")
+    return y

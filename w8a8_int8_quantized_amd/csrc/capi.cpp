@@ -1,0 +1,193 @@
+// extern "C" entry points of libw8a8.so (declared in include/w8a8.h).
+//
+// This layer only validates arguments and dispatches to the launchers; it
+// allocates nothing and never synchronises.  Every check runs on the host
+// before anything is enqueued, so a failed call leaves the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include "../../include/w8a8.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Common shape rule: rows >= 0, 0 <= K <= kMaxK, K % 128 == 0, rows * K < 2^40.
+int check_rows_k(int64_t R, int64_t K) {
+  if (R < 0 || K < 0 || R > kMaxRows || K > kMaxK || (K & 127) != 0) return W8_ERR_SHAPE;
+  if (R > 0 && K > 0 && R > kMaxElems / K) return W8_ERR_SHAPE;
+  return W8_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? W8_OK : W8_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_out(int y_dtype, bool allow_i32, w8::OutKind* out) {
+  switch (y_dtype) {
+    case W8_BF16: *out = w8::OUT_BF16; return W8_OK;
+    case W8_FP32: *out = w8::OUT_F32; return W8_OK;
+    case W8_I32:
+      if (!allow_i32) return W8_ERR_DTYPE;
+      *out = w8::OUT_I32;
+      return W8_OK;
+    default: return W8_ERR_DTYPE;
+  }
+}
+
+int check_gemm_common(const int8_t* A, const int8_t* W, const void* Y, int64_t M, int64_t N, int64_t K) {
+  int rc = check_rows_k(M, K);
+  if (rc) return rc;
+  rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (M > 0 && N > 0 && M > kMaxElems / N) return W8_ERR_SHAPE;
+  if (M == 0 || N == 0) return W8_OK;
+  if (!A || !W || !Y) return W8_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(W, 16) || !aligned(Y, 16)) return W8_ERR_ALIGN;
+  return W8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w8_abi_version(void) { return kAbiVersion; }
+
+const char* w8_status_string(int status) {
+  switch (status) {
+    case W8_OK: return "ok";
+    case W8_ERR_NULL: return "null pointer argument";
+    case W8_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or beyond the limits)";
+    case W8_ERR_ALIGN: return "misaligned pointer (data 16-byte, scales 4-byte)";
+    case W8_ERR_DTYPE: return "unsupported dtype";
+    case W8_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+static int quant_act_common(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* scale, bool group,
+                            void* stream) {
+  if (x_dtype != W8_BF16 && x_dtype != W8_FP16) return W8_ERR_DTYPE;
+  int rc = check_rows_k(M, K);
+  if (rc) return rc;
+  if (M == 0 || K == 0) return W8_OK;
+  if (!x || !q || !scale) return W8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return W8_ERR_ALIGN;
+  const bool fp16 = x_dtype == W8_FP16;
+  return status_of(group ? w8::launch_quant_group(x, fp16, M, K, q, scale, as_stream(stream))
+                         : w8::launch_quant_token(x, fp16, M, K, q, scale, as_stream(stream)));
+}
+
+int quant_act_group(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* scale, void* stream) {
+  return quant_act_common(x, x_dtype, M, K, q, scale, true, stream);
+}
+
+int quant_act_token(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* scale, void* stream) {
+  return quant_act_common(x, x_dtype, M, K, q, scale, false, stream);
+}
+
+int quant_weight_block(const void* w, int64_t N, int64_t K, int8_t* w_q, float* w_scale, void* stream) {
+  int rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (N == 0 || K == 0) return W8_OK;
+  if (!w || !w_q || !w_scale) return W8_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_quant_weight_block(w, N, K, w_q, w_scale, as_stream(stream)));
+}
+
+int requant_fp8_to_int8_block(const uint8_t* w_fp8, const float* scale_inv, int64_t N, int64_t K, int8_t* w_q,
+                              float* w_scale, uint16_t* w_bf16_or_null, void* stream) {
+  int rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (N == 0 || K == 0) return W8_OK;
+  if (!w_fp8 || !scale_inv || !w_q || !w_scale) return W8_ERR_NULL;
+  if (!aligned(w_fp8, 16) || !aligned(w_q, 16) || !aligned(scale_inv, 4) || !aligned(w_scale, 4) ||
+      (w_bf16_or_null && !aligned(w_bf16_or_null, 16)))
+    return W8_ERR_ALIGN;
+  return status_of(
+      w8::launch_requant_block(w_fp8, scale_inv, N, K, w_q, w_scale, w_bf16_or_null, as_stream(stream)));
+}
+
+int requant_fp8_to_int8_channel(const uint8_t* w_fp8, const float* scale_inv, int64_t N, int64_t K, int8_t* w_q,
+                                float* w_scale, void* stream) {
+  int rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (N == 0 || K == 0) return W8_OK;
+  if (!w_fp8 || !scale_inv || !w_q || !w_scale) return W8_ERR_NULL;
+  if (!aligned(w_fp8, 16) || !aligned(w_q, 16) || !aligned(scale_inv, 4) || !aligned(w_scale, 4))
+    return W8_ERR_ALIGN;
+  return status_of(w8::launch_requant_channel(w_fp8, scale_inv, N, K, w_q, w_scale, as_stream(stream)));
+}
+
+int gemm_w8a8_block(const int8_t* A, const float* a_scale, const int8_t* W, const float* w_scale, void* Y,
+                    int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  w8::OutKind out;
+  int rc = check_out(y_dtype, false, &out);
+  if (rc) return rc;
+  rc = check_gemm_common(A, W, Y, M, N, K);
+  if (rc || M == 0 || N == 0) return rc;
+  if (K == 0) return W8_ERR_SHAPE;
+  if (!a_scale || !w_scale) return W8_ERR_NULL;
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_gemm_block(A, a_scale, W, w_scale, Y, out, M, N, K, as_stream(stream)));
+}
+
+int gemm_w8a8_channel(const int8_t* A, const float* a_scale, const int8_t* W, const float* w_scale, void* Y,
+                      int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  w8::OutKind out;
+  int rc = check_out(y_dtype, true, &out);
+  if (rc) return rc;
+  rc = check_gemm_common(A, W, Y, M, N, K);
+  if (rc || M == 0 || N == 0) return rc;
+  if (K == 0 || K > (int64_t(1) << 17)) return W8_ERR_SHAPE;
+  if (out != w8::OUT_I32) {
+    if (!a_scale || !w_scale) return W8_ERR_NULL;
+    if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
+  }
+  return status_of(w8::launch_gemm_channel(A, a_scale, W, w_scale, Y, out, M, N, K, as_stream(stream)));
+}
+
+int gemm_w8a8_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
+                             void* stream) {
+  int rc = check_gemm_common(A, W, P, M, N, K);
+  if (rc || M == 0 || N == 0 || K == 0) return rc;
+  return status_of(w8::launch_gemm_block_partials(A, W, P, M, N, K, as_stream(stream)));
+}
+
+int gemm_w8a16_group(const uint16_t* x, const int8_t* W, const float* w_scale, uint16_t* Y, int64_t M, int64_t N,
+                     int64_t K, void* stream) {
+  int rc = check_rows_k(M, K);
+  if (rc) return rc;
+  rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (M > 0 && N > 0 && M > kMaxElems / N) return W8_ERR_SHAPE;
+  if (M == 0 || N == 0) return W8_OK;
+  if (K == 0) return W8_ERR_SHAPE;
+  if (!x || !W || !w_scale || !Y) return W8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(Y, 16) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_gemm_w8a16(x, W, w_scale, Y, M, N, K, as_stream(stream)));
+}
+
+int gemm_w8a8_block_grouped(const int8_t* A, const float* a_scale, const int8_t* W, const float* w_scale,
+                            const int32_t* expert_offsets, void* Y, int y_dtype, int64_t E, int64_t P, int64_t N,
+                            int64_t K, void* stream) {
+  w8::OutKind out;
+  int rc = check_out(y_dtype, false, &out);
+  if (rc) return rc;
+  if (E < 0 || E > 4096) return W8_ERR_SHAPE;
+  rc = check_gemm_common(A, W, Y, P, N, K);
+  if (rc || P == 0 || N == 0 || E == 0) return rc;
+  if (K == 0) return W8_ERR_SHAPE;
+  if (E > 0 && N * K > kMaxElems / E) return W8_ERR_SHAPE;
+  if (!a_scale || !w_scale || !expert_offsets) return W8_ERR_NULL;
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(expert_offsets, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_gemm_block_grouped(A, a_scale, W, w_scale, expert_offsets, Y, out, E, P, N, K,
+                                                 as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Internal launchers of libw8a8.so (host side).  Each enqueues its kernels on
+// the given stream and returns the launch status; argument checks are done by
+// the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8 {
+
+enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_I32 = 2 };
+
+hipError_t launch_quant_group(const void* x, bool fp16, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st);
+hipError_t launch_quant_token(const void* x, bool fp16, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st);
+hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int8_t* q, float* s, hipStream_t st);
+hipError_t launch_requant_block(const uint8_t* w, const float* si, int64_t N, int64_t K, int8_t* q, float* s,
+                                uint16_t* wbf, hipStream_t st);
+hipError_t launch_requant_channel(const uint8_t* w, const float* si, int64_t N, int64_t K, int8_t* q, float* s,
+                                  hipStream_t st);
+
+hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
+                               OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
+                             OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
+                                      hipStream_t st);
+hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
+                                     const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P, int64_t N,
+                                     int64_t K, hipStream_t st);
+hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
+                             int64_t K, hipStream_t st);
+
+// Small-M (decode) variants, used by the dispatchers above when M is small.
+hipError_t launch_gemm_block_decode(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
+                                    OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_gemm_channel_decode(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
+                                      OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
+}  // namespace w8

@@ -1,0 +1,365 @@
+// Quantisation kernels for gfx950: online activation quantisation (per
+// token-group and per token) and the offline weight conversions.
+//
+// Method: "DeepSeek R1 INT8 quantisation in SGLang" (Meituan), section 2.3:
+//   - block-wise scheme: 128 x 128 weight tiles, activations per token-group;
+//   - channel-wise scheme: one scale per output channel, activations per token;
+//   - offline: FP8 checkpoint -> BF16 -> INT8.
+// Quantiser: "FP8 vs INT8 quantisation for DeepSeek", section 3.2.1 (int8
+// branch): s = amax / 127, q = round(x / s) clamped to +-127.
+//
+// All kernels are HBM-streaming: every input byte is read once (the token
+// and tile quantisers keep their group in registers between the amax pass and
+// the quantise pass) and every output byte written once.
+#include "common.h"
+#include "launch.h"
+
+namespace w8 {
+namespace {
+
+// ------------------------------------------------------------------ decode
+// 8 values from a 16-byte chunk of bf16 or fp16.
+template <bool FP16>
+__device__ __forceinline__ void unpack8(const uint4& c, float* v) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (FP16) {
+      v[2 * i] = h2f(w[i] & 0xffffu);
+      v[2 * i + 1] = h2f(w[i] >> 16);
+    } else {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+}
+
+// OCP FP8-E4M3FN byte -> fp32, times 2^-120.  The 7 magnitude bits moved to
+// bit 20 form an fp32 whose exponent field is e and mantissa m/8:
+//   e >= 1: 2^(e-127) (1 + m/8)  = value * 2^-120
+//   e == 0: m/8 * 2^-126 (an fp32 subnormal) = value * 2^-120
+// so one exact multiply by 2^120 recovers the value.
+__device__ __forceinline__ float fp8_scaled_down(uint32_t byte_in_low_bits) {
+  uint32_t b = byte_in_low_bits & 0xffu;
+  uint32_t bits = ((b & 0x7fu) << 20) | ((b & 0x80u) << 24);
+  return __uint_as_float(bits);
+}
+
+constexpr float kTwo120 = 1.329227995784916e36f;   // 2^120, exact
+
+// fp32(decode(code) * scale_inv) rounded to bf16 (nearest even), returned
+// as the fp32 value of that bf16 and its 16-bit pattern.
+__device__ __forceinline__ float fp8_to_bf16_value(uint32_t byte, float scale_inv, uint32_t* bits16) {
+  float v = __fmul_rn(fp8_scaled_down(byte), kTwo120);        // exact decode
+  float p = __fmul_rn(v, scale_inv);
+  uint32_t h = f32_to_bf16_rne(p);
+  *bits16 = h;
+  return __uint_as_float(h << 16);
+}
+
+// 16 values (and their bf16 patterns) from a 16-byte chunk of FP8 codes.
+__device__ __forceinline__ void unpack16_fp8(const uint4& c, float scale_inv, float* v, uint32_t* bf) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * i + j] = fp8_to_bf16_value(w[i] >> (8 * j), scale_inv, &bf[4 * i + j]);
+}
+
+__device__ __forceinline__ float amax_n(const float* v, int n) {
+  float a = 0.f;
+  for (int i = 0; i < n; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+  return a;
+}
+
+// ------------------------------------------------------- per token-group
+// Each group of 128 values (256 bytes) is handled by 8 lanes, 16 values per
+// lane (two 16-byte loads), so one wave quantises 8 groups per round and a
+// 256-thread workgroup 32 groups per round, 2 rounds per workgroup.
+constexpr int kGroupRounds = 2;
+constexpr int kGroupsPerBlock = 32 * kGroupRounds;
+
+template <bool FP16>
+__global__ __launch_bounds__(256) void k_quant_group(const uint4* __restrict__ x, int8_t* __restrict__ q,
+                                                     float* __restrict__ scale, int64_t G) {
+  const int j = threadIdx.x & 7;
+  uint4 raw[kGroupRounds][2];
+  int64_t gidx[kGroupRounds];
+#pragma unroll
+  for (int r = 0; r < kGroupRounds; ++r) {
+    int64_t g = (int64_t)blockIdx.x * kGroupsPerBlock + r * 32 + (threadIdx.x >> 3);
+    gidx[r] = g;
+    int64_t gl = g < G ? g : G - 1;             // clamped: tail lanes load a valid group
+    const uint4* p = x + gl * 16 + 2 * j;       // 16 chunks of 16 B per group
+    raw[r][0] = p[0];
+    raw[r][1] = p[1];
+  }
+#pragma unroll
+  for (int r = 0; r < kGroupRounds; ++r) {
+    float v[16];
+    unpack8<FP16>(raw[r][0], v);
+    unpack8<FP16>(raw[r][1], v + 8);
+    float a = max8(amax_n(v, 16));
+    QScale sc = make_scale(a);
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = quant_one(v[i], sc);
+    if (gidx[r] < G) {
+      uint4 o;
+      o.x = pack4(t[0], t[1], t[2], t[3]);
+      o.y = pack4(t[4], t[5], t[6], t[7]);
+      o.z = pack4(t[8], t[9], t[10], t[11]);
+      o.w = pack4(t[12], t[13], t[14], t[15]);
+      reinterpret_cast<uint4*>(q + gidx[r] * 128)[j] = o;
+      if (j == 0) scale[gidx[r]] = sc.s;
+    }
+  }
+}
+
+// ------------------------------------------------------------ per row
+// One 256-thread workgroup per row.  A "chunk" is 16 input bytes: 8 bf16 /
+// fp16 values, or 16 FP8 codes.  The first CH chunks of every thread stay in
+// registers between the amax pass and the quantise pass; rows longer than
+// 256 * CH chunks re-read the rest (from L2) in the second pass.
+enum { FMT_BF16 = 0, FMT_FP16 = 1, FMT_FP8 = 2 };
+
+template <int FMT>
+struct RowFmt {
+  static constexpr int EPC = FMT == FMT_FP8 ? 16 : 8;   // elements per chunk
+};
+
+template <int FMT>
+__device__ __forceinline__ void chunk_values(const uint4& c, float si, float* v) {
+  if constexpr (FMT == FMT_FP8) {
+    uint32_t bf[16];
+    unpack16_fp8(c, si, v, bf);
+  } else {
+    unpack8<FMT == FMT_FP16>(c, v);
+  }
+}
+
+template <int FMT, int CH>
+__global__ __launch_bounds__(256) void k_quant_row(const uint4* __restrict__ x, const float* __restrict__ scale_inv,
+                                                   int8_t* __restrict__ q, float* __restrict__ scale, int K) {
+  constexpr int EPC = RowFmt<FMT>::EPC;
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nch = K / EPC;
+  const uint4* xr = x + row * (int64_t)nch;
+  // FP8 rows: scale_inv[row / 128][kb]; each 16-code chunk lies in one K block.
+  const float* sir = FMT == FMT_FP8 ? scale_inv + (row >> 7) * (int64_t)(K >> 7) : nullptr;
+  uint4 keep[CH];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    int c = threadIdx.x + 256 * i;
+    if (c < nch) keep[i] = xr[c];
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+      float v[EPC];
+      chunk_values<FMT>(keep[i], FMT == FMT_FP8 ? sir[(c * EPC) >> 7] : 0.f, v);
+      a = fmaxf(a, amax_n(v, EPC));
+    }
+  }
+  for (int c = threadIdx.x + 256 * CH; c < nch; c += 256) {
+    float v[EPC];
+    chunk_values<FMT>(xr[c], FMT == FMT_FP8 ? sir[(c * EPC) >> 7] : 0.f, v);
+    a = fmaxf(a, amax_n(v, EPC));
+  }
+  a = block_max256(a, red);
+  QScale sc = make_scale(a);
+  int8_t* qr = q + row * (int64_t)K;
+  auto emit = [&](const uint4& raw, int c) {
+    float v[EPC];
+    chunk_values<FMT>(raw, FMT == FMT_FP8 ? sir[(c * EPC) >> 7] : 0.f, v);
+    float t[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) t[e] = quant_one(v[e], sc);
+    if constexpr (EPC == 8) {
+      uint2 o;
+      o.x = pack4(t[0], t[1], t[2], t[3]);
+      o.y = pack4(t[4], t[5], t[6], t[7]);
+      reinterpret_cast<uint2*>(qr)[c] = o;
+    } else {
+      uint4 o;
+      o.x = pack4(t[0], t[1], t[2], t[3]);
+      o.y = pack4(t[4], t[5], t[6], t[7]);
+      o.z = pack4(t[8], t[9], t[10], t[11]);
+      o.w = pack4(t[12], t[13], t[14], t[15]);
+      reinterpret_cast<uint4*>(qr)[c] = o;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    int c = threadIdx.x + 256 * i;
+    if (c < nch) emit(keep[i], c);
+  }
+  for (int c = threadIdx.x + 256 * CH; c < nch; c += 256) emit(xr[c], c);
+  if (threadIdx.x == 0) scale[row] = sc.s;
+}
+
+// ---------------------------------------------------------- 128x128 tiles
+// One 256-thread workgroup per tile (grid x = kb, y = nb).
+// bf16 input: the tile is 128 rows x 256 bytes = 2048 chunks, 8 per thread:
+// thread t takes column chunk t & 15 of rows (t >> 4) + 16 i.
+__global__ __launch_bounds__(256) void k_quant_tile_bf16(const uint4* __restrict__ w, int8_t* __restrict__ q,
+                                                         float* __restrict__ scale, int N, int K) {
+  __shared__ float red[4];
+  const int KB = K >> 7;
+  const int kb = (int)(blockIdx.x % (unsigned)KB), nb = (int)(blockIdx.x / (unsigned)KB);
+  const int cc = threadIdx.x & 15;
+  const int nchr = K >> 3;   // 16-byte chunks per row
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int r = nb * 128 + (threadIdx.x >> 4) + 16 * i;
+    int rl = r < N ? r : N - 1;
+    raw[i] = w[(int64_t)rl * nchr + kb * 16 + cc];
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int r = nb * 128 + (threadIdx.x >> 4) + 16 * i;
+    float v[8];
+    unpack8<false>(raw[i], v);
+    if (r < N) a = fmaxf(a, amax_n(v, 8));
+  }
+  a = block_max256(a, red);
+  QScale sc = make_scale(a);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int r = nb * 128 + (threadIdx.x >> 4) + 16 * i;
+    float v[8], t[8];
+    unpack8<false>(raw[i], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = quant_one(v[e], sc);
+    if (r < N) {
+      uint2 o;
+      o.x = pack4(t[0], t[1], t[2], t[3]);
+      o.y = pack4(t[4], t[5], t[6], t[7]);
+      reinterpret_cast<uint2*>(q + (int64_t)r * K + kb * 128)[cc] = o;
+    }
+  }
+  if (threadIdx.x == 0) scale[(int64_t)nb * KB + kb] = sc.s;
+}
+
+// FP8 input: the tile is 128 rows x 128 bytes = 1024 chunks, 4 per thread:
+// thread t takes column chunk t & 7 of rows (t >> 3) + 32 i.
+template <bool WRITE_BF16>
+__global__ __launch_bounds__(256) void k_requant_tile_fp8(const uint4* __restrict__ w, const float* __restrict__ scale_inv,
+                                                          int8_t* __restrict__ q, float* __restrict__ scale,
+                                                          uint16_t* __restrict__ wbf, int N, int K) {
+  __shared__ float red[4];
+  const int KB = K >> 7;
+  const int kb = (int)(blockIdx.x % (unsigned)KB), nb = (int)(blockIdx.x / (unsigned)KB);
+  const int cc = threadIdx.x & 7;
+  const int nchr = K >> 4;
+  const float si = scale_inv[(int64_t)nb * KB + kb];
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int r = nb * 128 + (threadIdx.x >> 3) + 32 * i;
+    int rl = r < N ? r : N - 1;
+    raw[i] = w[(int64_t)rl * nchr + kb * 8 + cc];
+  }
+  float v[4][16];
+  uint32_t bf[4][16];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int r = nb * 128 + (threadIdx.x >> 3) + 32 * i;
+    unpack16_fp8(raw[i], si, v[i], bf[i]);
+    if (r < N) a = fmaxf(a, amax_n(v[i], 16));
+  }
+  a = block_max256(a, red);
+  QScale sc = make_scale(a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int r = nb * 128 + (threadIdx.x >> 3) + 32 * i;
+    float t[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[e] = quant_one(v[i][e], sc);
+    if (r < N) {
+      uint4 o;
+      o.x = pack4(t[0], t[1], t[2], t[3]);
+      o.y = pack4(t[4], t[5], t[6], t[7]);
+      o.z = pack4(t[8], t[9], t[10], t[11]);
+      o.w = pack4(t[12], t[13], t[14], t[15]);
+      reinterpret_cast<uint4*>(q + (int64_t)r * K + kb * 128)[cc] = o;
+      if (WRITE_BF16) {
+        uint4 b0, b1;
+        b0.x = bf[i][0] | (bf[i][1] << 16);   b0.y = bf[i][2] | (bf[i][3] << 16);
+        b0.z = bf[i][4] | (bf[i][5] << 16);   b0.w = bf[i][6] | (bf[i][7] << 16);
+        b1.x = bf[i][8] | (bf[i][9] << 16);   b1.y = bf[i][10] | (bf[i][11] << 16);
+        b1.z = bf[i][12] | (bf[i][13] << 16); b1.w = bf[i][14] | (bf[i][15] << 16);
+        uint4* dst = reinterpret_cast<uint4*>(wbf + (int64_t)r * K + kb * 128) + 2 * cc;
+        dst[0] = b0;
+        dst[1] = b1;
+      }
+    }
+  }
+  if (threadIdx.x == 0) scale[(int64_t)nb * KB + kb] = sc.s;
+}
+
+template <int FMT>
+hipError_t launch_row(const void* x, const float* si, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st) {
+  constexpr int EPC = RowFmt<FMT>::EPC;
+  const int64_t nch = K / EPC;
+  const uint4* xp = static_cast<const uint4*>(x);
+  dim3 grid((unsigned)M), block(256);
+  if (nch <= 256)
+    hipLaunchKernelGGL((k_quant_row<FMT, 1>), grid, block, 0, st, xp, si, q, s, (int)K);
+  else if (nch <= 512)
+    hipLaunchKernelGGL((k_quant_row<FMT, 2>), grid, block, 0, st, xp, si, q, s, (int)K);
+  else if (nch <= 1024)
+    hipLaunchKernelGGL((k_quant_row<FMT, 4>), grid, block, 0, st, xp, si, q, s, (int)K);
+  else if (nch <= 2048)
+    hipLaunchKernelGGL((k_quant_row<FMT, 8>), grid, block, 0, st, xp, si, q, s, (int)K);
+  else
+    hipLaunchKernelGGL((k_quant_row<FMT, 16>), grid, block, 0, st, xp, si, q, s, (int)K);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_group(const void* x, bool fp16, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st) {
+  const int64_t G = M * (K >> 7);
+  const int64_t blocks = (G + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  const uint4* xp = static_cast<const uint4*>(x);
+  if (fp16)
+    hipLaunchKernelGGL((k_quant_group<true>), dim3((unsigned)blocks), dim3(256), 0, st, xp, q, s, G);
+  else
+    hipLaunchKernelGGL((k_quant_group<false>), dim3((unsigned)blocks), dim3(256), 0, st, xp, q, s, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_token(const void* x, bool fp16, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st) {
+  return fp16 ? launch_row<FMT_FP16>(x, nullptr, M, K, q, s, st) : launch_row<FMT_BF16>(x, nullptr, M, K, q, s, st);
+}
+
+hipError_t launch_requant_channel(const uint8_t* w, const float* si, int64_t N, int64_t K, int8_t* q, float* s,
+                                  hipStream_t st) {
+  return launch_row<FMT_FP8>(w, si, N, K, q, s, st);
+}
+
+hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int8_t* q, float* s, hipStream_t st) {
+  dim3 grid((unsigned)((K >> 7) * ((N + 127) >> 7)));
+  hipLaunchKernelGGL(k_quant_tile_bf16, grid, dim3(256), 0, st, static_cast<const uint4*>(w), q, s, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_block(const uint8_t* w, const float* si, int64_t N, int64_t K, int8_t* q, float* s,
+                                uint16_t* wbf, hipStream_t st) {
+  dim3 grid((unsigned)((K >> 7) * ((N + 127) >> 7)));
+  const uint4* wp = reinterpret_cast<const uint4*>(w);
+  if (wbf)
+    hipLaunchKernelGGL((k_requant_tile_fp8<true>), grid, dim3(256), 0, st, wp, si, q, s, wbf, (int)N, (int)K);
+  else
+    hipLaunchKernelGGL((k_requant_tile_fp8<false>), grid, dim3(256), 0, st, wp, si, q, s, wbf, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+}  // namespace w8
