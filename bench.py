@@ -1,0 +1,356 @@
+"""Benchmark of the W8A8 INT8 linear-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-rows] [--no-cpu]
+
+Headline step (the DeepSeek-V3 dense MLP at M = 4096 tokens, channel-wise
+scheme, inputs resident in HBM):
+    quant_act_token(x[4096, 7168])  -> gemm_w8a8_channel(gate_up: K=7168 -> N=36864)
+    quant_act_token(h[4096, 18432]) -> gemm_w8a8_channel(down:    K=18432 -> N=7168)
+The intermediate h is a separate synthetic input (the SiLU-and-multiply
+between the two GEMMs is not part of the method).  Two weight sets alternate
+between steps.  value = int8 GEMM operations of the step / step time, in TOPS.
+
+Also reported (unless --no-rows): every other row of the path at its own
+shapes - block-wise GEMMs and quantisers at M = 4096, channel-wise at
+M = 128 and 1024, decode (M = 1..64) block-wise and W8A16 GEMMs in GB/s over
+weight copies rotated through more than 1 GB so the 256 MB Infinity Cache
+cannot serve repeats, the grouped MoE GEMMs, and the FP8 requantisation.
+
+roofline: the dominant kernel (the gate_up channel GEMM), timed with HIP
+events on the stream it runs on, against the dense int8 MFMA peak of 5.0 POP/s.
+cpu_baseline: the CPU oracle (numpy) on a bounded sample of the same step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, 8 TB/s
+M_HEAD = 4096
+GATE_UP = (7168, 36864)       # (K, N)
+DOWN = (18432, 7168)
+
+# traffic of the dominant kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
+# scaled by the same counters' reading for a copy kernel of known size; None
+# until counters have been taken for the current kernel.
+TRAFFIC_GATE_UP_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="headline step only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rows-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_calls(fn, n_rot, reps, warm=3):
+    """Average ms per call of fn(i) over reps calls, i cycling over n_rot buffers."""
+    import torch
+    for i in range(warm):
+        fn(i % n_rot)
+    torch.cuda.synchronize()
+    a, b = _events()
+    a.record()
+    for i in range(reps):
+        fn(i % n_rot)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def headline(args):
+    import torch
+    import synth
+    import w8a8_int8_quantized_amd as w8
+
+    dev = torch.device("cuda:0")
+    seed = synth.SEEDS["channel"]
+    (Kg, Ng), (Kd, Nd) = GATE_UP, DOWN
+    x = synth.activations(M_HEAD, Kg, seed=seed, device=dev)
+    h = synth.activations(M_HEAD, Kd, seed=seed + 10, device=dev)
+    sets = []
+    for s in range(2):
+        wg = synth.weights(Ng, Kg, seed=seed + 20 + s, device=dev)
+        wd = synth.weights(Nd, Kd, seed=seed + 30 + s, device=dev)
+        sets.append((w8.quant_weight_channel(wg), w8.quant_weight_channel(wd)))
+        del wg, wd
+    qx = (torch.empty(M_HEAD, Kg, dtype=torch.int8, device=dev), torch.empty(M_HEAD, dtype=torch.float32, device=dev))
+    qh = (torch.empty(M_HEAD, Kd, dtype=torch.int8, device=dev), torch.empty(M_HEAD, dtype=torch.float32, device=dev))
+    yg = torch.empty(M_HEAD, Ng, dtype=torch.bfloat16, device=dev)
+    yd = torch.empty(M_HEAD, Nd, dtype=torch.bfloat16, device=dev)
+    ev = []
+
+    def step(i, record=False):
+        (wg_q, wg_s), (wd_q, wd_s) = sets[i % 2]
+        w8.quant_act_token(x, out=qx)
+        if record:
+            a, b = _events()
+            a.record()
+        w8.gemm_w8a8_channel(qx[0], qx[1], wg_q, wg_s, out=yg)
+        if record:
+            b.record()
+            ev.append((a, b))
+        w8.quant_act_token(h, out=qh)
+        w8.gemm_w8a8_channel(qh[0], qh[1], wd_q, wd_s, out=yd)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, record=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    ops = 2.0 * M_HEAD * (Ng * Kg + Nd * Kd)
+    tops = ops / (ms * 1e-3) / 1e12
+    k_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    k_tops = 2.0 * M_HEAD * Ng * Kg / (k_ms * 1e-3) / 1e12
+    # per-kernel split of one step (events around each call)
+    parts = {}
+    for name, fn in (("quant_act_token_x", lambda i: w8.quant_act_token(x, out=qx)),
+                     ("gemm_channel_gate_up", lambda i: w8.gemm_w8a8_channel(qx[0], qx[1], sets[i][0][0], sets[i][0][1], out=yg)),
+                     ("quant_act_token_h", lambda i: w8.quant_act_token(h, out=qh)),
+                     ("gemm_channel_down", lambda i: w8.gemm_w8a8_channel(qh[0], qh[1], sets[i][1][0], sets[i][1][1], out=yd))):
+        parts[name] = round(time_calls(fn, 2, 10), 4)
+    del sets
+    torch.cuda.empty_cache()
+    return ms, tops, k_ms, k_tops, parts
+
+
+def rows(args):
+    """Every other row of the path at its own shapes."""
+    import torch
+    import synth
+    import w8a8_int8_quantized_amd as w8
+
+    dev = torch.device("cuda:0")
+    R = args.rows_reps
+    out = {}
+
+    def gemm_entry(ms, M, N, K, wbytes):
+        ops = 2.0 * M * N * K
+        byts = wbytes + M * K + 2 * M * N
+        return {"ms": round(ms, 4), "TOPS": round(ops / ms / 1e9, 1),
+                "mfma_frac": round(ops / ms / 1e9 / PEAK_INT8_TOPS, 3),
+                "GBps": round(byts / ms / 1e6, 1), "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+
+    # --- quantisers at M = 4096, K = 7168 (bytes: 2 in + 1 out + scales)
+    x = synth.activations(4096, 7168, seed=2, device=dev)
+    ms = time_calls(lambda i: w8.quant_act_group(x), 1, R)
+    b = 4096 * 7168 * 3 + 4096 * 56 * 4
+    out["quant_act_group_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                        "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    ms = time_calls(lambda i: w8.quant_act_token(x), 1, R)
+    b = 4096 * 7168 * 3 + 4096 * 4
+    out["quant_act_token_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                        "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+
+    # --- block-wise at M = 4096 (DeepSeek-V3 shapes), weights FP8 -> requantised
+    qa_cache = {}
+    for name in ("gate_up", "down", "q_a", "q_b", "kv_a"):
+        K, N = synth.SHAPES[name]
+        codes, si = synth.fp8_weights(N, K, seed=synth.SEEDS["block"], device=dev)
+        if name == "gate_up":
+            ms = time_calls(lambda i: w8.requant_fp8_to_int8_block(codes, si), 1, 5)
+            b = N * K * 2
+            out["requant_fp8_block_gate_up"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                                "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+        wq, ws = w8.requant_fp8_to_int8_block(codes, si)
+        del codes
+        if K not in qa_cache:
+            xa = synth.activations(4096, K, seed=synth.SEEDS["block"] + 1, device=dev)
+            qa_cache[K] = w8.quant_act_group(xa)
+            del xa
+        qa, sa = qa_cache[K]
+        y = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wq, ws, out=y), 1, max(5, R // 2))
+        out[f"gemm_block_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
+        if name in ("gate_up", "down"):
+            qt = w8.quant_act_token(synth.activations(4096, K, seed=5, device=dev))
+            wqc, wsc = w8.quant_act_token(synth.weights(N, K, seed=6, device=dev))
+            ms = time_calls(lambda i: w8.gemm_w8a8_channel(qt[0], qt[1], wqc, wsc, out=y), 1, max(5, R // 2))
+            out[f"gemm_channel_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
+            for M in (128, 1024):
+                yq = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+                a0, a1 = qt[0][:M].contiguous(), qt[1][:M].contiguous()
+                ms = time_calls(lambda i: w8.gemm_w8a8_channel(a0, a1, wqc, wsc, out=yq), 1, R)
+                out[f"gemm_channel_m{M}_{name}"] = gemm_entry(ms, M, N, K, N * K)
+            del wqc, wsc, qt
+        del wq, ws, y
+    del qa_cache
+    torch.cuda.empty_cache()
+
+    # --- decode block-wise: M in {1, 8, 32, 64}, K = 7168, N = 36864, 4 weight copies (1.06 GB)
+    K, N = GATE_UP
+    wsets = []
+    for s in range(4):
+        w = synth.weights(N, K, seed=synth.SEEDS["decode"] + s, device=dev)
+        wsets.append(w8.quant_weight_block(w))
+        del w
+    for M in (1, 8, 32, 64):
+        qa, sa = w8.quant_act_group(synth.activations(M, K, seed=M, device=dev))
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wsets[i][0], wsets[i][1], out=y), 4, R)
+        e = gemm_entry(ms, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
+        out[f"decode_block_m{M}"] = e
+    del wsets
+    torch.cuda.empty_cache()
+
+    # --- decode W8A16: Qwen3-8B-shaped linears, 20 weight copies (> 1 GB)
+    for name in ("w8a16_qkv", "w8a16_down"):
+        K, N = synth.SHAPES[name]
+        ws_ = []
+        for s in range(20):
+            w = synth.weights(N, K, seed=40 + s, device=dev, dtype=torch.float16)
+            ws_.append(w8.quant_act_group(w))
+            del w
+        for M in (1, 8, 32, 64):
+            xx = synth.activations(M, K, seed=M, device=dev, dtype=torch.float16)
+            y = torch.empty(M, N, dtype=torch.float16, device=dev)
+            ms = time_calls(lambda i: w8.gemm_w8a16_group(xx, ws_[i][0], ws_[i][1], out=y), 20, R)
+            byts = N * K + 4 * N * (K // 128) + 2 * M * K + 2 * M * N
+            out[f"decode_w8a16_{name}_m{M}"] = {"ms": round(ms, 4), "GBps": round(byts / ms / 1e6, 1),
+                                                "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+        del ws_
+    torch.cuda.empty_cache()
+
+    # --- MoE: 256 experts, top-8 of 4096 tokens
+    E, T, TOPK = 256, 4096, 8
+    logits = synth.router_logits(T, E, seed=synth.SEEDS["moe"], device=dev)
+    rows_, _, offs = synth.route_topk(logits, TOPK)
+    P = rows_.numel()
+    for name in ("moe_gate_up", "moe_down"):
+        K, N = synth.SHAPES[name]
+        NB, KB = (N + 127) // 128, K // 128
+        Wq = torch.empty(E, N, K, dtype=torch.int8, device=dev)
+        Ws = torch.empty(E, NB, KB, dtype=torch.float32, device=dev)
+        for e0 in range(0, E, 32):
+            w = synth.weights(32 * N, K, seed=100 + e0, device=dev)
+            q, s = w8.quant_weight_block(w)
+            Wq[e0:e0 + 32] = q.view(32, N, K)
+            Ws[e0:e0 + 32] = s.view(32, NB, KB)
+            del w, q, s
+        if name == "moe_gate_up":
+            xt = synth.activations(T, K, seed=7, device=dev)
+            qa, sa = w8.quant_act_group(xt[rows_].contiguous())
+            del xt
+        else:
+            qa, sa = w8.quant_act_group(synth.activations(P, K, seed=8, device=dev))
+        y = torch.empty(P, N, dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: w8.gemm_w8a8_block_grouped(qa, sa, Wq, Ws, offs, out=y), 1, 5, warm=1)
+        ops = 2.0 * P * N * K
+        byts = E * N * K + P * K + 2 * P * N
+        out[f"gemm_block_grouped_{name}"] = {"ms": round(ms, 4), "TOPS": round(ops / ms / 1e9, 1),
+                                             "GBps": round(byts / ms / 1e6, 1),
+                                             "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+        del Wq, Ws, qa, sa, y
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline():
+    """The CPU oracle as it stands on a bounded sample of the headline step:
+    1024 of the 4096 tokens and a quarter of the output channels of both
+    GEMMs (per-token and per-channel quantisation are row-local, so the sample
+    computes exactly what the full step computes for those rows/columns)."""
+    import numpy as np
+    import synth
+    from oracle import gemm as ogemm, quant as oquant
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:                                           # pragma: no cover
+        cores = os.cpu_count()
+    Ms = 1024
+    (Kg, Ng), (Kd, Nd) = GATE_UP, DOWN
+    Ngs, Nds = Ng // 4, Nd // 4
+    seed = synth.SEEDS["channel"]
+    x = synth.to_numpy(synth.activations(Ms, Kg, seed=seed))
+    h = synth.to_numpy(synth.activations(Ms, Kd, seed=seed + 10))
+    wg = oquant.quant_act_token(synth.to_numpy(synth.weights(Ngs, Kg, seed=seed + 20)))
+    wd = oquant.quant_act_token(synth.to_numpy(synth.weights(Nds, Kd, seed=seed + 30)))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        qa, sa = oquant.quant_act_token(x)
+        ogemm.gemm_channel(qa, sa, wg[0], wg[1])
+        qh, sh = oquant.quant_act_token(h)
+        ogemm.gemm_channel(qh, sh, wd[0], wd[1])
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    ops = 2.0 * Ms * (Ngs * Kg + Nds * Kd)
+    return {"value": round(ops / t / 1e12, 4), "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"channel-wise MLP step on {Ms} of 4096 tokens and 1/4 of the output channels "
+                      f"(gate_up N={Ngs}, down N={Nds}); median of 3 runs of {t:.2f} s",
+            "seconds": round(t, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] headline: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    ms, tops, k_ms, k_tops, parts = headline(args)
+    print(f"[bench] headline {ms:.3f} ms/step, {tops:.1f} TOPS; gate_up kernel {k_ms:.3f} ms", file=sys.stderr,
+          flush=True)
+    extra = {}
+    if not args.no_rows:
+        print("[bench] rows", file=sys.stderr, flush=True)
+        extra = rows(args)
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+    Kg, Ng = GATE_UP
+    traffic = TRAFFIC_GATE_UP_BYTES
+    line = {
+        "metric": "int8 GEMM TOPS and % of MI355X int8 peak (M=4096); decode GB/s % HBM",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "DeepSeek-V3 dense MLP, channel-wise W8A8: per-token quant + gate_up "
+                               "(K=7168 -> N=36864) + per-token quant + down (K=18432 -> N=7168)",
+                   "M": M_HEAD, "gate_up": [Kg, Ng], "down": list(DOWN), "out_dtype": "bf16",
+                   "parallelism": "1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(k_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(k_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_w8a8_channel gate_up M=4096", "kernel_ms": round(k_ms, 4)},
+        "cpu_baseline": cpu,
+        "step_parts_ms": parts,
+        "rows": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
