@@ -1,101 +1,31 @@
-// Large-M INT8 GEMMs on gfx950 int8 MFMA (v_mfma_i32_16x16x64_i8).
+// Large-M INT8 GEMMs on gfx950 int8 MFMA.
 //
 // Method: "DeepSeek R1 INT8 quantisation in SGLang" (Meituan), section 2.3
 // and its Figure 3.
-//   channel-wise: Y = (A . W^T) * a_scale[m] * w_scale[n], one dequant in the
-//                 epilogue after an all-integer K loop;
+//   channel-wise: Y = (A . W^T) * a_scale[m] * w_scale[n]: an all-integer K
+//                 loop, one dequantisation in the epilogue;
 //   block-wise:   the int32 partial of every 128-wide K block is dequantised
 //                 with a_scale[m][kb] * w_scale[n/128][kb] and accumulated in
 //                 fp32 inside the K loop.
 //
-// Tiling (all operands K-contiguous, one 128-byte K block per pipeline stage):
-//   * global -> registers -> LDS, two LDS stages (the load of block kb+1 is in
-//     flight while block kb is multiplied), one barrier per K block;
-//   * LDS rows are 128 bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 7)
-//     so the 8 lanes that read one ds_read_b128 phase hit 8 distinct bank groups;
-//   * MFMA operand A is a 16-row slice of W and operand B a 16-row slice of the
-//     activations, so each lane's 4 accumulators are 4 consecutive output
-//     columns n of one output row m: contiguous 8/16-byte stores, one
-//     activation scale per lane and fragment, and (block-wise) one weight
-//     scale per wave since a wave's 128 columns lie in one 128-wide N block;
-//   * workgroup ids are remapped so that each XCD (ids congruent mod 8) works
-//     on a contiguous band of tiles, grouped 8 tiles tall in M, which keeps the
-//     A and W panels it streams in its own L2.
-#include "common.h"
+// Data path (see pipeline.h): K blocks of 128 bytes per row stream
+// global -> LDS through direct-to-LDS buffer loads into a two-slot ring; the
+// load of block kb+1 is in flight while block kb is multiplied.  MFMA operand
+// A is a slice of W and operand B a slice of the activations, so each lane's
+// accumulators are consecutive output columns n of one output row m:
+// contiguous stores, one activation scale per lane and fragment, and (block
+// scheme) one weight scale per wave, because a wave's 128 columns lie inside
+// one 128-wide N block.
 #include "launch.h"
+#include "pipeline.h"
 
 namespace w8 {
 namespace {
 
-constexpr int kBlockK = 128;
-
-__device__ __forceinline__ int lane_off(int lane, int ks) {
-  return (lane & 15) * 128 + ((((ks << 2) | (lane >> 4)) ^ (lane & 7)) << 4);
-}
-
-// Global -> registers: ROWS x 128 bytes of the K block kb, NT threads, 16 bytes
-// per load.  Thread t loads column chunk t & 7 of rows (t >> 3) + (NT/8) i.
-// Rows at or past rows_valid are clamped to the last valid row: they only feed
-// output rows/columns that are never stored.
-template <int ROWS, int NT>
-__device__ __forceinline__ void g2r(const int8_t* __restrict__ tile, int K, int rows_valid, int kb, uint4* reg) {
-  constexpr int PER = ROWS * 8 / NT;
-  const char* b = reinterpret_cast<const char*>(tile) + kb * kBlockK + (threadIdx.x & 7) * 16;
-  const int r0 = threadIdx.x >> 3;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    int r = r0 + (NT / 8) * i;
-    r = r < rows_valid ? r : rows_valid - 1;
-    reg[i] = *reinterpret_cast<const uint4*>(b + r * K);
-  }
-}
-
-template <int ROWS, int NT>
-__device__ __forceinline__ void r2s(char* lds, const uint4* reg) {
-  constexpr int PER = ROWS * 8 / NT;
-  const int c = threadIdx.x & 7;
-  const int r0 = threadIdx.x >> 3;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    int r = r0 + (NT / 8) * i;
-    *reinterpret_cast<uint4*>(lds + r * 128 + ((c ^ (r & 7)) << 4)) = reg[i];
-  }
-}
-
-__device__ __forceinline__ v4i frag(const char* lds, int row_base, int loff) {
-  return *reinterpret_cast<const v4i*>(lds + row_base * 128 + loff);
-}
-
-__device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-
-struct Tile {
-  int tm, tn;
-};
-
-// XCD-aware tile order: the hardware places workgroup b on XCD b % 8; tiles
-// [x*T/8, (x+1)*T/8) go to XCD x, and inside that band tiles run 8 tall in M.
-__device__ __forceinline__ Tile map_tile(int b, int TM, int TN) {
-  const int T = TM * TN;
-  const int x = b & 7, j = b >> 3;
-  const int T8 = T >> 3, rem = T & 7;
-  const int t = x * T8 + (x < rem ? x : rem) + j;
-  constexpr int GM = 8;
-  const int per = GM * TN;
-  const int g = t / per;
-  const int first = g * GM;
-  const int gm = TM - first < GM ? TM - first : GM;
-  const int r = t - g * per;
-  Tile tl;
-  tl.tm = first + r % gm;
-  tl.tn = r / gm;
-  return tl;
-}
-
 // Store 4 consecutive outputs Y[m][n..n+3] (n multiple of 4).
 template <int OUT>
-__device__ __forceinline__ void store4(void* Y, int64_t idx, int n, int N, bool vec, float a, float b, float c, float d) {
+__device__ __forceinline__ void store4(void* Y, int64_t idx, int n, int N, bool vec, float a, float b, float c,
+                                       float d) {
   if (OUT == OUT_F32) {
     float* y = static_cast<float*>(Y) + idx;
     if (vec && n + 3 < N) {
@@ -108,7 +38,8 @@ __device__ __forceinline__ void store4(void* Y, int64_t idx, int n, int N, bool 
     }
   } else {
     uint16_t* y = static_cast<uint16_t*>(Y) + idx;
-    uint32_t ha = f32_to_bf16_rne(a), hb = f32_to_bf16_rne(b), hc = f32_to_bf16_rne(c), hd = f32_to_bf16_rne(d);
+    const uint32_t ha = f32_to_bf16_rne(a), hb = f32_to_bf16_rne(b), hc = f32_to_bf16_rne(c),
+                   hd = f32_to_bf16_rne(d);
     if (vec && n + 3 < N) {
       *reinterpret_cast<uint2*>(y) = make_uint2(ha | (hb << 16), hc | (hd << 16));
     } else {
@@ -132,25 +63,37 @@ __device__ __forceinline__ void store4i(int32_t* y, int n, int N, bool vec, v4i 
 }
 
 // ------------------------------------------------------------ channel-wise
-// 256 x 256 output tile, 4 waves in a 2 (n) x 2 (m) grid, 128 x 128 per wave
-// (8 x 8 MFMA fragments, 256 int32 accumulators per lane).
+// 256 x 256 output tile per workgroup, 4 waves in a 2 (n) x 2 (m) grid, each
+// wave 128 x 128 (8 x 8 fragments of v_mfma_i32_16x16x64_i8, 256 int32
+// accumulators per lane in AGPRs).  An LDS slot holds one K block:
+// A 256 x 128 B then W 256 x 128 B.  The loop runs over 64-wide K steps; the
+// fragments of step t+1 are read from LDS while step t's 64 MFMAs run, and
+// every second step (a K block boundary) waits for the next block's DMA,
+// synchronises, and starts the DMA of the block after it.
 constexpr int kChBM = 256, kChBN = 256;
+constexpr int kChStage = (kChBM + kChBN) * 128;
 
 template <int OUT>
 __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                         void* __restrict__ Y, int M, int N, int K, int TM, int TN) {
-  __shared__ __attribute__((aligned(16))) char smem[2][(kChBM + kChBN) * 128];
-  const Tile tl = map_tile(blockIdx.x, TM, TN);
-  const int m0 = tl.tm * kChBM, n0 = tl.tn * kChBN;
+                                                         void* __restrict__ Y, int M, int N, int K, int TM) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kChStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  const int8_t* Ab = A + (int64_t)m0 * K;
-  const int8_t* Wb = W + (int64_t)n0 * K;
+  // consecutive workgroups walk down M first: they share the W panel in L2
+  const int tm = blockIdx.x % TM, tn = blockIdx.x / TM;
+  const int m0 = tm * kChBM, n0 = tn * kChBN;
   const int mval = M - m0 < kChBM ? M - m0 : kChBM;
   const int nval = N - n0 < kChBN ? N - n0 : kChBN;
-  const int KB = K >> 7;
+  const v4i ra = make_rsrc(A + (int64_t)m0 * K, (uint32_t)(mval * K));
+  const v4i rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(nval * K));
+  const int voff = wave * 64 * K + dma_lane_off(lane, K);   // wave fills tile rows 64*wave .. +63
+  const uint32_t lds0 = lds_addr(smem);
+  const int NK = K >> 7;
+  const int K8 = 8 * K;
+  const int lo0 = frag_off(lane & 15, lane >> 4);           // 16x16x64 operand: row l%16, chunk l/16
+  const int lo1 = frag_off(lane & 15, 4 + (lane >> 4));
 
   v4i acc[8][8];
 #pragma unroll
@@ -158,41 +101,56 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
-  uint4 ra[8], rw[8];
-  g2r<kChBM, 256>(Ab, K, mval, 0, ra);
-  g2r<kChBN, 256>(Wb, K, nval, 0, rw);
-  r2s<kChBM, 256>(smem[0], ra);
-  r2s<kChBN, 256>(smem[0] + kChBM * 128, rw);
-  __syncthreads();
-  const int lo0 = lane_off(lane, 0), lo1 = lane_off(lane, 1);
-
-  for (int kb = 0; kb < KB; ++kb) {
-    const char* cur = smem[kb & 1];
-    const bool more = kb + 1 < KB;
-    if (more) {
-      g2r<kChBM, 256>(Ab, K, mval, kb + 1, ra);
-      g2r<kChBN, 256>(Wb, K, nval, kb + 1, rw);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int lo = ks ? lo1 : lo0;
-      v4i wf[8], af[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wf[i] = frag(cur + kChBM * 128, wn * 128 + i * 16, lo);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) af[j] = frag(cur, wm * 128 + j * 16, lo);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma(wf[i], af[j], acc[i][j]);
-    }
-    if (more) {
-      char* nxt = smem[(kb + 1) & 1];
-      r2s<kChBM, 256>(nxt, ra);
-      r2s<kChBN, 256>(nxt + kChBM * 128, rw);
-    }
-    __syncthreads();
+#define CH_DMA(T)                                                                                  \
+  {                                                                                               \
+    const uint32_t base = lds0 + ((T) & 1) * kChStage + wave * 8192;                              \
+    _Pragma("unroll") for (int b = 0; b < 8; ++b) dma16(ra, voff, b * K8 + (T) * 128, base + b * 1024); \
+    _Pragma("unroll") for (int b = 0; b < 8; ++b)                                                 \
+      dma16(rw, voff, b * K8 + (T) * 128, base + kChBM * 128 + b * 1024);                         \
   }
+#define CH_RD(KS, WF, AF)                                                                          \
+  {                                                                                               \
+    const char* buf = smem + (((KS) >> 1) & 1) * kChStage;                                        \
+    const int lo = ((KS) & 1) ? lo1 : lo0;                                                        \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) AF[j] = *(const v4i*)(buf + (wm * 128 + j * 16) * 128 + lo); \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                 \
+      WF[i] = *(const v4i*)(buf + kChBM * 128 + (wn * 128 + i * 16) * 128 + lo);                  \
+  }
+
+  CH_DMA(0)
+  waitcnt<0, 15>();
+  barrier();
+  if (1 < NK) CH_DMA(1)
+  v4i wc[8], ac[8];
+  CH_RD(0, wc, ac)
+  for (int t = 0; t < 2 * NK; ++t) {
+    if (t & 1) {
+      // step t+1 opens K block (t+1)/2, whose DMA was started two steps ago
+      waitcnt<0, 0>();
+      barrier();
+      if (((t + 1) >> 1) + 1 < NK) CH_DMA(((t + 1) >> 1) + 1)
+    }
+    v4i wn_[8], an_[8];
+    CH_RD(t + 1, wn_, an_)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wc[i], ac[j], acc[i][j], 0, 0, 0);
+    // one LDS read for the next step after every 4 MFMAs
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wc[i] = wn_[i];
+      ac[i] = an_[i];
+    }
+  }
+#undef CH_DMA
+#undef CH_RD
+  waitcnt<0, 15>();
 
   const bool vec = (N & 3) == 0;
 #pragma unroll
@@ -219,25 +177,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
 }
 
 // -------------------------------------------------------------- block-wise
-// 128 (m) x 256 (n) output tile, 4 waves in a 2 (n) x 2 (m) grid, 64 (m) x
-// 128 (n) per wave.  Per K block each fragment pair is two chained MFMAs from
-// zero (the exact int32 partial P), then acc += (a_scale * w_scale) * P on the
-// VALU, interleaved with the next fragment's MFMAs.
-constexpr int kBkBM = 128, kBkBN = 256;
+// 256 (n) x BM (m) output tile, BM = 64 * NWM; 2 * NWM waves in a 2 (n) x NWM
+// (m) grid, each wave 128 (n) x 64 (m) as 4 x 2 fragments of
+// v_mfma_i32_32x32x32_i8.  Per K block each fragment is four chained MFMAs
+// from zero (the exact int32 partial P of that block), then
+// acc += (a_scale * w_scale) * P on the VALU; acc stays in VGPRs.  With
+// NWM = 4 two waves share each SIMD, so one wave's dequantisation overlaps
+// the other's MFMAs.
 enum { MODE_DEQUANT = 0, MODE_PARTIALS = 1, MODE_GROUPED = 2 };
 
-// For the grouped GEMM: find which (expert, 128-row slice) this workgroup's
-// linear m-tile index falls in.  Each expert e owns rows [off[e], off[e+1]) of
-// the expert-sorted activations and ceil(count / 128) m-tiles.
+// Grouped GEMM: find the (expert, BM-row slice) of this workgroup's linear
+// m-tile index.  Expert e owns rows [off[e], off[e+1]) of the expert-sorted
+// activations and ceil(count / BM) m-tiles; offsets are clamped to [0, P]
+// so that no contract violation can cause an out-of-bounds access.
 struct GroupTile {
-  int e, r0, r1;   // expert and row range of this tile; e < 0: no tile
+  int e, r0, r1;   // e < 0: no tile for this workgroup
 };
 
+template <int BM>
 __device__ GroupTile grouped_lookup(const int32_t* __restrict__ off, int E, int P, int tmg) {
   __shared__ int scan[256];
   __shared__ int sel[3];
   const int t = threadIdx.x;
-  const int ept = (E + 255) >> 8;
+  const int nt = blockDim.x;
+  const int ept = (E + nt - 1) / nt;
   const int e0 = t * ept;
   const int e1 = e0 + ept < E ? e0 + ept : E;
   int cnt = 0;
@@ -245,30 +208,30 @@ __device__ GroupTile grouped_lookup(const int32_t* __restrict__ off, int E, int 
     int lo = off[e], hi = off[e + 1];
     lo = lo < 0 ? 0 : (lo > P ? P : lo);
     hi = hi < lo ? lo : (hi > P ? P : hi);
-    cnt += (hi - lo + kBkBM - 1) / kBkBM;
+    cnt += (hi - lo + BM - 1) / BM;
   }
   if (t == 0) sel[0] = -1;
-  scan[t] = cnt;
+  if (t < 256) scan[t] = cnt;
   __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    int v = t >= d ? scan[t - d] : 0;
+  for (int d = 1; d < nt; d <<= 1) {
+    const int v = (t < 256 && t >= d) ? scan[t - d] : 0;
     __syncthreads();
-    scan[t] += v;
+    if (t < 256) scan[t] += v;
     __syncthreads();
   }
-  const int excl = scan[t] - cnt;
-  if (tmg >= excl && tmg < excl + cnt) {
+  const int excl = (t < 256 ? scan[t] : 0) - cnt;
+  if (t < 256 && tmg >= excl && tmg < excl + cnt) {
     int acc = excl;
     for (int e = e0; e < e1; ++e) {
       int lo = off[e], hi = off[e + 1];
       lo = lo < 0 ? 0 : (lo > P ? P : lo);
       hi = hi < lo ? lo : (hi > P ? P : hi);
-      int c = (hi - lo + kBkBM - 1) / kBkBM;
+      const int c = (hi - lo + BM - 1) / BM;
       if (tmg < acc + c) {
-        int r0 = lo + (tmg - acc) * kBkBM;
+        const int r0 = lo + (tmg - acc) * BM;
         sel[0] = e;
         sel[1] = r0;
-        sel[2] = r0 + kBkBM < hi ? r0 + kBkBM : hi;
+        sel[2] = r0 + BM < hi ? r0 + BM : hi;
         break;
       }
       acc += c;
@@ -282,12 +245,16 @@ __device__ GroupTile grouped_lookup(const int32_t* __restrict__ off, int E, int 
   return g;
 }
 
-template <int MODE, int OUT>
-__global__ __launch_bounds__(256, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
-                                                       const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                       const int32_t* __restrict__ offsets, void* __restrict__ Y,
-                                                       int M, int N, int K, int TM, int TN, int E) {
-  __shared__ __attribute__((aligned(16))) char smem[2][(kBkBM + kBkBN) * 128];
+template <int MODE, int OUT, int NWM>
+__global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
+                                                             const int8_t* __restrict__ W, const float* __restrict__ sw,
+                                                             const int32_t* __restrict__ offsets, void* __restrict__ Y,
+                                                             int M, int N, int K, int TM, int TN, int E) {
+  constexpr int BM = 64 * NWM, BN = 256, NWV = 2 * NWM;
+  constexpr int STG = (BM + BN) * 128;
+  constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A (= 4)
+  constexpr int WI = BN / (8 * NWV);   // ... and for W
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STG];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
@@ -299,113 +266,136 @@ __global__ __launch_bounds__(256, 1) void k_gemm_block(const int8_t* __restrict_
   const float* swx = sw;
   if (MODE == MODE_GROUPED) {
     const int tmg = blockIdx.x / TN;
-    n0 = (blockIdx.x - tmg * TN) * kBkBN;
-    GroupTile g = grouped_lookup(offsets, E, M, tmg);
+    n0 = (blockIdx.x - tmg * TN) * BN;
+    const GroupTile g = grouped_lookup<BM>(offsets, E, M, tmg);
     if (g.e < 0) return;
     m0 = g.r0;
     mrows = g.r1 - g.r0;
     Wx = W + (int64_t)g.e * N * K;
     swx = sw + (int64_t)g.e * NB * KB;
   } else {
-    const Tile tl = map_tile(blockIdx.x, TM, TN);
-    m0 = tl.tm * kBkBM;
-    n0 = tl.tn * kBkBN;
-    mrows = M - m0 < kBkBM ? M - m0 : kBkBM;
+    const int tm = blockIdx.x % TM, tn = blockIdx.x / TM;
+    m0 = tm * BM;
+    n0 = tn * BN;
+    mrows = M - m0 < BM ? M - m0 : BM;
   }
-  const int nval = N - n0 < kBkBN ? N - n0 : kBkBN;
-  const int8_t* Ab = A + (int64_t)m0 * K;
-  const int8_t* Wb = Wx + (int64_t)n0 * K;
+  const int nval = N - n0 < BN ? N - n0 : BN;
+  const v4i ra = make_rsrc(A + (int64_t)m0 * K, (uint32_t)(mrows * K));
+  const v4i rw = make_rsrc(Wx + (int64_t)n0 * K, (uint32_t)(nval * K));
+  const int voffA = wave * AI * 8 * K + dma_lane_off(lane, K);
+  const int voffW = wave * WI * 8 * K + dma_lane_off(lane, K);
+  const uint32_t lds0 = lds_addr(smem);
+  const int K8 = 8 * K;
+  int lo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) lo[ks] = frag_off(lane & 31, 2 * ks + (lane >> 5));   // 32x32x32 operand
 
   // this wave's 128 columns lie in one 128-wide N block
   int nbw = (n0 + wn * 128) >> 7;
   nbw = nbw < NB ? nbw : NB - 1;
   const float* sw_row = swx + (int64_t)nbw * KB;
-  // the activation rows of this lane's 4 m-fragments (clamped for loads)
-  int mrow[4];
+  const float* sa_row[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int r = wm * 64 + j * 16 + (lane & 15);
-    mrow[j] = m0 + (r < mrows ? r : mrows - 1);
+  for (int j = 0; j < 2; ++j) {
+    const int r = wm * 64 + j * 32 + (lane & 31);
+    sa_row[j] = sa + (int64_t)(m0 + (r < mrows ? r : mrows - 1)) * KB;
   }
 
-  v4f facc[8][4];
+  v4f facc[4][2][4];
   if (MODE != MODE_PARTIALS) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) facc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) facc[i][j][g] = (v4f){0.f, 0.f, 0.f, 0.f};
   }
 
-  uint4 ra[4], rw[8];
-  g2r<kBkBM, 256>(Ab, K, mrows, 0, ra);
-  g2r<kBkBN, 256>(Wb, K, nval, 0, rw);
-  r2s<kBkBM, 256>(smem[0], ra);
-  r2s<kBkBN, 256>(smem[0] + kBkBM * 128, rw);
-  __syncthreads();
-  const int lo0 = lane_off(lane, 0), lo1 = lane_off(lane, 1);
-  const bool vec = (N & 3) == 0;
+#define BK_DMA(T)                                                                                  \
+  {                                                                                               \
+    const uint32_t base = lds0 + ((T) & 1) * STG;                                                 \
+    _Pragma("unroll") for (int b = 0; b < AI; ++b)                                                \
+      dma16(ra, voffA, b * K8 + (T) * 128, base + (wave * AI + b) * 1024);                        \
+    _Pragma("unroll") for (int b = 0; b < WI; ++b)                                                \
+      dma16(rw, voffW, b * K8 + (T) * 128, base + BM * 128 + (wave * WI + b) * 1024);             \
+  }
 
+  const bool vec = (N & 3) == 0;
+  BK_DMA(0)
   for (int kb = 0; kb < KB; ++kb) {
-    const char* cur = smem[kb & 1];
-    const bool more = kb + 1 < KB;
-    if (more) {
-      g2r<kBkBM, 256>(Ab, K, mrows, kb + 1, ra);
-      g2r<kBkBN, 256>(Wb, K, nval, kb + 1, rw);
-    }
-    float s[4];
+    waitcnt<0, 0>();                  // block kb landed (own loads); own reads of kb-1 done
+    barrier();                        // everyone's block kb landed; everyone is past kb-1
+    if (kb + 1 < KB) BK_DMA(kb + 1)   // into the slot kb-1 used
+    const char* buf = smem + (kb & 1) * STG;
+    float s[2];
     if (MODE != MODE_PARTIALS) {
       const float swv = sw_row[kb];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = __fmul_rn(sa[(int64_t)mrow[j] * KB + kb], swv);
+      for (int j = 0; j < 2; ++j) s[j] = __fmul_rn(sa_row[j][kb], swv);
     }
-    v4i wf0[8], wf1[8], af0[4], af1[4];
+    v4i af[2][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      wf0[i] = frag(cur + kBkBM * 128, wn * 128 + i * 16, lo0);
-      wf1[i] = frag(cur + kBkBM * 128, wn * 128 + i * 16, lo1);
-    }
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      af0[j] = frag(cur, wm * 64 + j * 16, lo0);
-      af1[j] = frag(cur, wm * 64 + j * 16, lo1);
-    }
+      for (int ks = 0; ks < 4; ++ks) af[j][ks] = *(const v4i*)(buf + (wm * 64 + j * 32) * 128 + lo[ks]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < 4; ++i) {
+      v4i wf[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v4i p = mfma(wf0[i], af0[j], (v4i){0, 0, 0, 0});
-        p = mfma(wf1[i], af1[j], p);
+      for (int ks = 0; ks < 4; ++ks) wf[ks] = *(const v4i*)(buf + BM * 128 + (wn * 128 + i * 32) * 128 + lo[ks]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        v16i p = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) p = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[ks], af[j][ks], p, 0, 0, 0);
         if (MODE == MODE_PARTIALS) {
-          const int m = m0 + wm * 64 + j * 16 + (lane & 15);
-          const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
-          if (m < M && n < N) store4i(static_cast<int32_t*>(Y) + ((int64_t)kb * M + m) * N + n, n, N, vec, p);
+          const int ml = wm * 64 + j * 32 + (lane & 31);
+          if (ml < mrows) {
+            const int m = m0 + ml;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int n = n0 + wn * 128 + i * 32 + g * 8 + 4 * (lane >> 5);
+              if (n < N)
+                store4i(static_cast<int32_t*>(Y) + ((int64_t)kb * M + m) * N + n, n, N, vec,
+                        (v4i){p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]});
+            }
+          }
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) facc[i][j][r] = __builtin_fmaf(s[j], (float)p[r], facc[i][j][r]);
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              facc[i][j][g][r] = __builtin_fmaf(s[j], (float)p[4 * g + r], facc[i][j][g][r]);
         }
       }
     }
-    if (more) {
-      char* nxt = smem[(kb + 1) & 1];
-      r2s<kBkBM, 256>(nxt, ra);
-      r2s<kBkBN, 256>(nxt + kBkBM * 128, rw);
-    }
-    __syncthreads();
   }
+#undef BK_DMA
+  waitcnt<0, 15>();
 
   if (MODE == MODE_PARTIALS) return;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ml = wm * 64 + j * 16 + (lane & 15);
+  for (int j = 0; j < 2; ++j) {
+    const int ml = wm * 64 + j * 32 + (lane & 31);
     if (ml >= mrows) continue;
     const int m = m0 + ml;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
-      if (n >= N) continue;
-      store4<OUT>(Y, (int64_t)m * N + n, n, N, vec, facc[i][j][0], facc[i][j][1], facc[i][j][2], facc[i][j][3]);
-    }
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + i * 32 + g * 8 + 4 * (lane >> 5);
+        if (n >= N) continue;
+        store4<OUT>(Y, (int64_t)m * N + n, n, N, vec, facc[i][j][g][0], facc[i][j][g][1], facc[i][j][g][2],
+                    facc[i][j][g][3]);
+      }
   }
+}
+
+template <int MODE, int OUT, int NWM>
+void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float* sa, const int8_t* W,
+                         const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E) {
+  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM>), grid, dim3(128 * NWM), 0, st, A, sa, W, sw, off, Y, M, N, K, TM,
+                     TN, E);
 }
 
 }  // namespace
@@ -417,13 +407,13 @@ hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W
   dim3 grid((unsigned)(TM * TN)), block(256);
   switch (out) {
     case OUT_BF16:
-      hipLaunchKernelGGL((k_gemm_channel<OUT_BF16>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM, TN);
+      hipLaunchKernelGGL((k_gemm_channel<OUT_BF16>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM);
       break;
     case OUT_F32:
-      hipLaunchKernelGGL((k_gemm_channel<OUT_F32>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM, TN);
+      hipLaunchKernelGGL((k_gemm_channel<OUT_F32>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM);
       break;
     default:
-      hipLaunchKernelGGL((k_gemm_channel<OUT_I32>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM, TN);
+      hipLaunchKernelGGL((k_gemm_channel<OUT_I32>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM);
       break;
   }
   return hipGetLastError();
@@ -432,22 +422,30 @@ hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W
 hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                              OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (M <= 64) return launch_gemm_block_decode(A, sa, W, sw, Y, out, M, N, K, st);
-  const int TM = (int)((M + kBkBM - 1) / kBkBM), TN = (int)((N + kBkBN - 1) / kBkBN);
-  dim3 grid((unsigned)(TM * TN)), block(256);
-  if (out == OUT_BF16)
-    hipLaunchKernelGGL((k_gemm_block<MODE_DEQUANT, OUT_BF16>), grid, block, 0, st, A, sa, W, sw, nullptr, Y, (int)M,
-                       (int)N, (int)K, TM, TN, 0);
-  else
-    hipLaunchKernelGGL((k_gemm_block<MODE_DEQUANT, OUT_F32>), grid, block, 0, st, A, sa, W, sw, nullptr, Y, (int)M,
-                       (int)N, (int)K, TM, TN, 0);
+  const int TN = (int)((N + 255) / 256);
+  if (M <= 128) {
+    const int TM = (int)((M + 127) / 128);
+    dim3 grid((unsigned)(TM * TN));
+    if (out == OUT_BF16)
+      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+    else
+      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+  } else {
+    const int TM = (int)((M + 255) / 256);
+    dim3 grid((unsigned)(TM * TN));
+    if (out == OUT_BF16)
+      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 4>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+    else
+      launch_block_kernel<MODE_DEQUANT, OUT_F32, 4>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
                                       hipStream_t st) {
-  const int TM = (int)((M + kBkBM - 1) / kBkBM), TN = (int)((N + kBkBN - 1) / kBkBN);
-  hipLaunchKernelGGL((k_gemm_block<MODE_PARTIALS, OUT_I32>), dim3((unsigned)(TM * TN)), dim3(256), 0, st, A, nullptr,
-                     W, nullptr, nullptr, P, (int)M, (int)N, (int)K, TM, TN, 0);
+  const int TM = (int)((M + 255) / 256), TN = (int)((N + 255) / 256);
+  launch_block_kernel<MODE_PARTIALS, OUT_I32, 4>(dim3((unsigned)(TM * TN)), st, A, nullptr, W, nullptr, nullptr, P,
+                                                 (int)M, (int)N, (int)K, TM, TN, 0);
   return hipGetLastError();
 }
 
@@ -455,15 +453,15 @@ hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int
                                      const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P, int64_t N,
                                      int64_t K, hipStream_t st) {
   // upper bound on the number of 128-row m-tiles over all experts
-  const int64_t TMmax = (P + kBkBM - 1) / kBkBM + E;
-  const int TN = (int)((N + kBkBN - 1) / kBkBN);
-  dim3 grid((unsigned)(TMmax * TN)), block(256);
+  const int64_t TMmax = (P + 127) / 128 + E;
+  const int TN = (int)((N + 255) / 256);
+  dim3 grid((unsigned)(TMmax * TN));
   if (out == OUT_BF16)
-    hipLaunchKernelGGL((k_gemm_block<MODE_GROUPED, OUT_BF16>), grid, block, 0, st, A, sa, W, sw, offsets, Y, (int)P,
-                       (int)N, (int)K, (int)TMmax, TN, (int)E);
+    launch_block_kernel<MODE_GROUPED, OUT_BF16, 2>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
+                                                   (int)TMmax, TN, (int)E);
   else
-    hipLaunchKernelGGL((k_gemm_block<MODE_GROUPED, OUT_F32>), grid, block, 0, st, A, sa, W, sw, offsets, Y, (int)P,
-                       (int)N, (int)K, (int)TMmax, TN, (int)E);
+    launch_block_kernel<MODE_GROUPED, OUT_F32, 2>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
+                                                  (int)TMmax, TN, (int)E);
   return hipGetLastError();
 }
 
