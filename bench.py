@@ -39,7 +39,7 @@ DOWN = (18432, 7168)
 # traffic of the dominant kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
 # scaled by the same counters' reading for a copy kernel of known size; None
 # until counters have been taken for the current kernel.
-TRAFFIC_GATE_UP_BYTES = None
+TRAFFIC_GATE_UP_BYTES = 2.682e9   # rocprofv3 FETCH_SIZE x2.000 + WRITE_SIZE x1.000 (copy-calibrated), per launch
 
 
 def parse():
@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rows-reps", type=int, default=20)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 times): the reference kernel of known "
+                         "size for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -311,6 +314,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calib:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": src.numel() * 4}))
+        return
     print(f"[bench] headline: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
     ms, tops, k_ms, k_tops, parts = headline(args)
     print(f"[bench] headline {ms:.3f} ms/step, {tops:.1f} TOPS; gate_up kernel {k_ms:.3f} ms", file=sys.stderr,
