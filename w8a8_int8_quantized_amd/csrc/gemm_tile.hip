@@ -62,6 +62,19 @@ __device__ __forceinline__ void store4i(int32_t* y, int n, int N, bool vec, v4i 
   }
 }
 
+// Workgroup -> tile.  The hardware dispatches workgroup b to XCD b % 8, and
+// each XCD has its own L2.  Tiles t = x*T/8 .. (x+1)*T/8 - 1 (M fastest) go
+// to XCD x, so an XCD owns a contiguous band of N tiles: every W panel is
+// pulled into one L2 only, and the XCD's concurrent workgroups share it.
+__device__ __forceinline__ void xcd_tile(int b, int TM, int TN, int& tm, int& tn) {
+  const int T = TM * TN;
+  const int x = b & 7, j = b >> 3;
+  const int T8 = T >> 3, rem = T & 7;
+  const int t = x * T8 + (x < rem ? x : rem) + j;
+  tm = t % TM;
+  tn = t / TM;
+}
+
 // ------------------------------------------------------------ channel-wise
 // 256 x 256 output tile per workgroup, 4 waves in a 2 (n) x 2 (m) grid, each
 // wave 128 x 128 (8 x 8 fragments of v_mfma_i32_16x16x64_i8, 256 int32
@@ -81,8 +94,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  // consecutive workgroups walk down M first: they share the W panel in L2
-  const int tm = blockIdx.x % TM, tn = blockIdx.x / TM;
+  int tm, tn;
+  xcd_tile(blockIdx.x, TM, (int)gridDim.x / TM, tm, tn);
   const int m0 = tm * kChBM, n0 = tn * kChBN;
   const int mval = M - m0 < kChBM ? M - m0 : kChBM;
   const int nval = N - n0 < kChBN ? N - n0 : kChBN;
@@ -274,7 +287,8 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     Wx = W + (int64_t)g.e * N * K;
     swx = sw + (int64_t)g.e * NB * KB;
   } else {
-    const int tm = blockIdx.x % TM, tn = blockIdx.x / TM;
+    int tm, tn;
+    xcd_tile(blockIdx.x, TM, TN, tm, tn);
     m0 = tm * BM;
     n0 = tn * BN;
     mrows = M - m0 < BM ? M - m0 : BM;
