@@ -116,6 +116,50 @@ def test_w8a16_group(M, N, K):
     assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
 
 
+# Decode shapes wide enough for the workgroup-shared activation kernels: each
+# N makes a different workgroup width (3, 4, 6, 8 and 9 waves of 16 columns)
+# the one whose grid splits evenly over the CUs, and is 8 columns short of a
+# whole number of workgroups, so the last wave is ragged.  K = 640 is five K
+# blocks: two full staging groups of two blocks and a half-empty third.
+DECODE_WIDE_N = [12280, 16376, 24568, 32760, 36856]
+
+
+@pytest.mark.parametrize("N", DECODE_WIDE_N)
+@pytest.mark.parametrize("M", [1, 24, 64])
+def test_decode_wide_block_and_channel(M, N):
+    K = 640
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M + N, scheme="block")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    _, y64, y32 = gemm.gemm_block(qa, sa, qw, sw)
+    yf = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    e32 = gemm.normwise_rel_err(_np(yf), y32)
+    assert e32 <= 1e-5 and gemm.normwise_rel_err(_np(yf), y64) <= TOL64, e32
+    yb = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M + N + 7, scheme="channel")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    ACC, _, y32 = gemm.gemm_channel(qa, sa, qw, sw)
+    assert np.array_equal(_np(w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)), ACC)
+    yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
+    assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
+    yb = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+
+
+@pytest.mark.parametrize("M", [1, 24, 64, 80])
+def test_w8a16_wide(M):
+    N, K = 12280, 640
+    x = synth.activations(M, K, seed=M + 3, dtype=torch.float16)
+    w = synth.weights(N, K, seed=N + M, dtype=torch.float16)
+    qw, sw = quant.quant_act_group(w.numpy())
+    y64, y32 = gemm.gemm_w8a16_group(x.numpy(), qw, sw)
+    X, W, SW = _dev(x.numpy(), qw, sw)
+    yn = _np(w8.gemm_w8a16_group(X, W, SW)).astype(np.float32)
+    e32, e64 = gemm.normwise_rel_err(yn, y32), gemm.normwise_rel_err(yn, y64)
+    assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+
+
 def test_grouped_moe_gemm_with_empty_experts():
     E, T, topk, K, N = 12, 200, 2, 512, 384
     lg = synth.router_logits(T, E, seed=4).numpy()

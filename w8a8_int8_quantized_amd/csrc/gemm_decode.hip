@@ -3,10 +3,13 @@
 // With M <= 64 the weights dominate the traffic (N x K bytes against M x K of
 // activations), so these kernels are HBM-bound: every weight byte is loaded
 // once, straight from global memory into MFMA operand registers (no LDS
-// staging), with the next K block's loads in flight while the current one is
-// multiplied.  A workgroup owns 16 * FNW output columns; its SK waves split
-// the K blocks between them (block kb goes to wave kb % SK) and their partial
-// results are summed in LDS in wave order, so results are deterministic.
+// staging).  A workgroup owns 16 * FNW output columns; its SK waves split the
+// K blocks between them (block kb goes to wave kb % SK), and each wave keeps
+// PF blocks of loads in flight in a register ring.  SK is chosen per call so
+// that every workgroup of the grid is resident at once (no tail wave of
+// workgroups) with as many loads in flight as the register budget allows.
+// The per-wave partial results are summed in LDS in wave order, so results
+// are deterministic.
 //
 // Method references:
 //   W8A8 block-wise / channel-wise: "DeepSeek R1 INT8 quantisation in SGLang"
@@ -15,45 +18,97 @@
 //   (symmetric group-wise INT8 weights, fp16 activations).
 #include "common.h"
 #include "launch.h"
+#include "pipeline.h"
 
 namespace w8 {
 namespace {
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ v4i ld16(const int8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+// SIMDs per GPU the dispatchers size grids against (256 CUs x 4).
+constexpr int kSimds = 256 * 4;
+constexpr int kCUs = 256;
+
+// Store 4 consecutive outputs of row m (n multiple of 4).
+template <int OUT>
+__device__ __forceinline__ void store_out4(void* Y, int64_t idx, int n, int N, bool vec, const float* o) {
+  if (OUT == OUT_F32) {
+    float* y = static_cast<float*>(Y) + idx;
+    if (vec && n + 3 < N) {
+      *reinterpret_cast<float4*>(y) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) y[r] = o[r];
+    }
+  } else {
+    uint16_t* y = static_cast<uint16_t*>(Y) + idx;
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(o[r]);
+    if (vec && n + 3 < N) {
+      *reinterpret_cast<uint2*>(y) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) y[r] = (uint16_t)h[r];
+    }
+  }
+}
+
+// Branch-free loads.  Every operand is read through a raw buffer descriptor
+// whose range ends at the last valid byte; a load past it returns zero and
+// moves no data.  Rows past M or N fall outside their descriptor by
+// construction, and the K blocks past the end of a wave's share get the
+// offset kOob added (beyond every range used here: a descriptor spans at most
+// 64 rows x 2^20 columns x 2 bytes).  No load sits under a branch, so the
+// compiler keeps the whole prefetch ring in flight (a branch around a load
+// makes it wait for every outstanding load at the join).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x40000000u;
+
+__device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i bl16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float blf(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
 
 // --------------------------------------------------------------- W8A8
 // MODE 0: block-wise (fp32 accumulate of per-block dequantised partials);
 // MODE 1: channel-wise (int32 accumulate over all K, one epilogue dequant).
-template <int MODE, int MF, int FNW, int SK, int OUT>
+// Fragment layout (v_mfma_i32_16x16x64_i8 with W as operand A): lane l holds
+// weight row n0 + 16 f + (l & 15) and activation row 16 j + (l & 15), K bytes
+// 16 q .. 16 q + 15 (q = l >> 4) of each 64-wide half of the K block; the
+// result lane holds columns n0 + 16 f + 4 q + r (r = 0..3) of row 16 j + (l & 15).
+template <int MODE, int MF, int FNW, int SK, int PF, int OUT>
 __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                          void* __restrict__ Y, int M, int N, int K) {
-  __shared__ v4i red[SK][FNW][MF][64];
+  __shared__ v4i red[SK][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int n0 = blockIdx.x * 16 * FNW;
   const int KB = K >> 7;
+  const int rows = N - n0 < 16 * FNW ? N - n0 : 16 * FNW;
 
-  const int8_t* wrow[FNW];
-  int nb[FNW];
+  // W rows n0 .. n0 + rows - 1; the workgroup's columns lie in one 128-row
+  // weight block (16 * FNW divides 128), so its block scales are one row of sw.
+  const rsrc_t rw = rsrc(W + (int64_t)n0 * K, (int64_t)rows * K);
+  const rsrc_t ra = rsrc(A, (int64_t)M * K);
+  const rsrc_t rsw = rsrc(sw + (int64_t)(n0 >> 7) * KB, (int64_t)KB * 4);
+  const rsrc_t rsa = rsrc(sa, (int64_t)M * KB * 4);
+  uint32_t woff[FNW], aoff[MF], saoff[MF];
 #pragma unroll
-  for (int f = 0; f < FNW; ++f) {
-    int n = n0 + f * 16 + (lane & 15);
-    n = n < N ? n : N - 1;
-    wrow[f] = W + (int64_t)n * K + q * 16;
-    int b = (n0 + f * 16) >> 7;
-    nb[f] = b;
-  }
-  const int8_t* arow[MF];
-  bool aval[MF];
+  for (int f = 0; f < FNW; ++f) woff[f] = (uint32_t)((f * 16 + (lane & 15)) * K + q * 16);
 #pragma unroll
   for (int j = 0; j < MF; ++j) {
-    int m = j * 16 + (lane & 15);
-    aval[j] = m < M;
-    arow[j] = A + (int64_t)(m < M ? m : M - 1) * K + q * 16;
+    aoff[j] = (uint32_t)((j * 16 + (lane & 15)) * K + q * 16);
+    saoff[j] = (uint32_t)((j * 16 + (lane & 15)) * KB * 4);
   }
 
   v4f facc[FNW][MF];
@@ -66,138 +121,305 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restric
       iacc[f][j] = (v4i){0, 0, 0, 0};
     }
 
-  v4i wv[FNW][2], av[MF][2];
-  int kb = wave;
-  if (kb < KB) {
+  // register ring: PF K blocks in flight per wave
+  v4i wv[PF][FNW][2], av[PF][MF][2];
+  float ssa[PF][MF], ssw[PF][FNW];
+  auto load = [&](int P, int kb) {
+    const uint32_t ko = kb < KB ? (uint32_t)kb * 128u : kOob;
+    const uint32_t so = kb < KB ? (uint32_t)kb * 4u : kOob;
 #pragma unroll
     for (int f = 0; f < FNW; ++f) {
-      wv[f][0] = ld16(wrow[f] + kb * 128);
-      wv[f][1] = ld16(wrow[f] + kb * 128 + 64);
+      wv[P][f][0] = bl16(rw, woff[f] + ko);
+      wv[P][f][1] = bl16(rw, woff[f] + ko + 64);
+      if (MODE == 0) ssw[P][f] = blf(rsw, so);
     }
 #pragma unroll
     for (int j = 0; j < MF; ++j) {
-      av[j][0] = ld16(arow[j] + kb * 128);
-      av[j][1] = ld16(arow[j] + kb * 128 + 64);
+      av[P][j][0] = bl16(ra, aoff[j] + ko);
+      av[P][j][1] = bl16(ra, aoff[j] + ko + 64);
+      if (MODE == 0) ssa[P][j] = blf(rsa, saoff[j] + so);
     }
+  };
+  // the prologue issues the slots in ring order (the scheduler would reverse
+  // them, and the loop would then wait for the whole ring on every pass)
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    load(p, wave + p * SK);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  for (; kb < KB; kb += SK) {
-    v4i cw[FNW][2], ca[MF][2];
+  // this wave's K blocks: wave, wave + SK, ...; PF of them per iteration, the
+  // slots past the end hold zeros
+  const int nb = (KB - wave + SK - 1) / SK;
+  const int iters = (nb + PF - 1) / PF;
+  for (int it = 0; it < iters; ++it) {
+    const int kb0 = wave + it * SK * PF;
 #pragma unroll
-    for (int f = 0; f < FNW; ++f) {
-      cw[f][0] = wv[f][0];
-      cw[f][1] = wv[f][1];
-    }
-#pragma unroll
-    for (int j = 0; j < MF; ++j) {
-      ca[j][0] = aval[j] ? av[j][0] : (v4i){0, 0, 0, 0};
-      ca[j][1] = aval[j] ? av[j][1] : (v4i){0, 0, 0, 0};
-    }
-    const int kn = kb + SK;
-    if (kn < KB) {
-#pragma unroll
-      for (int f = 0; f < FNW; ++f) {
-        wv[f][0] = ld16(wrow[f] + kn * 128);
-        wv[f][1] = ld16(wrow[f] + kn * 128 + 64);
-      }
-#pragma unroll
-      for (int j = 0; j < MF; ++j) {
-        av[j][0] = ld16(arow[j] + kn * 128);
-        av[j][1] = ld16(arow[j] + kn * 128 + 64);
-      }
-    }
-    if (MODE == 0) {
-      float s[FNW][MF];
-#pragma unroll
-      for (int f = 0; f < FNW; ++f) {
-        const int bb = nb[f] < ((N + 127) >> 7) ? nb[f] : ((N + 127) >> 7) - 1;
-        const float swv = sw[(int64_t)bb * KB + kb];
-#pragma unroll
-        for (int j = 0; j < MF; ++j) {
-          int m = j * 16 + (lane & 15);
-          m = m < M ? m : M - 1;
-          s[f][j] = __fmul_rn(sa[(int64_t)m * KB + kb], swv);
-        }
-      }
+    for (int p = 0; p < PF; ++p) {
+      // consume slot p, then refill it with the block SK * PF further on;
+      // the other PF - 1 slots stay in flight meanwhile
 #pragma unroll
       for (int f = 0; f < FNW; ++f)
 #pragma unroll
         for (int j = 0; j < MF; ++j) {
-          v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(cw[f][0], ca[j][0], (v4i){0, 0, 0, 0}, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_i32_16x16x64_i8(cw[f][1], ca[j][1], p, 0, 0, 0);
+          if (MODE == 0) {
+            v4i pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], av[p][j][0], (v4i){0, 0, 0, 0}, 0, 0, 0);
+            pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], av[p][j][1], pp, 0, 0, 0);
+            const float s = __fmul_rn(ssa[p][j], ssw[p][f]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(s[f][j], (float)p[r], facc[f][j][r]);
+            for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(s, (float)pp[r], facc[f][j][r]);
+          } else {
+            iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], av[p][j][0], iacc[f][j], 0, 0, 0);
+            iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], av[p][j][1], iacc[f][j], 0, 0, 0);
+          }
         }
-    } else {
-#pragma unroll
-      for (int f = 0; f < FNW; ++f)
-#pragma unroll
-        for (int j = 0; j < MF; ++j) {
-          iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cw[f][0], ca[j][0], iacc[f][j], 0, 0, 0);
-          iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cw[f][1], ca[j][1], iacc[f][j], 0, 0, 0);
-        }
+      load(p, kb0 + p * SK + SK * PF);
+      // keep slot p's consumers here: hoisted above the refills of earlier
+      // slots they would make the wave wait for the whole ring
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // cross-wave reduction in wave order
+  // cross-wave reduction, one fragment at a time, summed in wave order
+  const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int f = 0; f < FNW; ++f)
 #pragma unroll
-    for (int j = 0; j < MF; ++j)
-      red[wave][f][j][lane] = MODE == 0 ? __builtin_bit_cast(v4i, facc[f][j]) : iacc[f][j];
-  __syncthreads();
-  if (wave != 0) return;
+    for (int j = 0; j < MF; ++j) {
+      red[wave][lane] = MODE == 0 ? __builtin_bit_cast(v4i, facc[f][j]) : iacc[f][j];
+      __syncthreads();
+      if (wave == ((f * MF + j) % SK)) {
+        const int n = n0 + f * 16 + 4 * q;
+        const int m = j * 16 + (lane & 15);
+        if (n < N && m < M) {
+          float o[4];
+          if (MODE == 0) {
+            v4f t = __builtin_bit_cast(v4f, red[0][lane]);
+#pragma unroll
+            for (int w = 1; w < SK; ++w) t += __builtin_bit_cast(v4f, red[w][lane]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = t[r];
+            store_out4<OUT>(Y, (int64_t)m * N + n, n, N, vec, o);
+          } else {
+            v4i t = red[0][lane];
+#pragma unroll
+            for (int w = 1; w < SK; ++w) t += red[w][lane];
+            if (OUT == OUT_I32) {
+              int32_t* y = static_cast<int32_t*>(Y) + (int64_t)m * N + n;
+              if (vec && n + 3 < N) {
+                *reinterpret_cast<v4i*>(y) = t;
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (n + r < N) y[r] = t[r];
+              }
+            } else {
+              const float s_m = sa[m];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[r] = n + r < N ? __fmul_rn((float)t[r], __fmul_rn(s_m, sw[n + r])) : 0.f;
+              store_out4<OUT>(Y, (int64_t)m * N + n, n, N, vec, o);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// --------------------------------------------------------------- W8A8, shared activations
+// Same contraction and fragment layout as k_decode_w8a8, organised so that
+// the activations are loaded once per workgroup rather than once per wave:
+// the workgroup's NWV waves own
+// 16 adjacent columns each and walk the same K blocks.  The activations move
+// in groups of G K blocks: while the waves multiply group g out of one LDS
+// buffer, group g + 1 (already in registers) is written to the other and
+// group g + 2 is loaded; one barrier per group.  Stage layout: G blocks of
+// 16 MF rows x 128 bytes, row r's 16-byte chunk c stored at c ^ (r & 7), so
+// fragment reads are conflict-free.  Weights stream straight into registers
+// through a G-deep ring.  No cross-wave reduction: every wave covers all of K
+// for its columns.  The dispatcher sizes workgroups so that the grid splits
+// evenly over the CUs (the weight stream runs at the pace of the most loaded
+// CU).
+template <int MODE, int MF, int NWV, int G, int OUT>
+__global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __restrict__ A, const float* __restrict__ sa,
+                                                        const int8_t* __restrict__ W, const float* __restrict__ sw,
+                                                        void* __restrict__ Y, int M, int N, int K) {
+  constexpr int FNW = 1;
+  constexpr int ROWS = 16 * MF;                                  // activation rows per block
+  constexpr int CHUNKS = ROWS * 8;                               // 16-byte chunks per block
+  constexpr int NT = 64 * NWV;                                   // threads
+  constexpr int AG = (G * CHUNKS + NT - 1) / NT;                 // chunks per thread per group
+  constexpr int SG = (G * ROWS + NT - 1) / NT;                   // block scales per thread per group
+  __shared__ v4i as[2][G * CHUNKS];
+  __shared__ float ss[2][G * ROWS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4;
+  const int n0 = blockIdx.x * 16 * FNW * NWV;
+  const int nw = n0 + 16 * FNW * wave;
+  const int KB = K >> 7;
+  const int NG = (KB + G - 1) / G;
+  int rows = N - nw;
+  rows = rows < 0 ? 0 : (rows > 16 * FNW ? 16 * FNW : rows);
+
+  // a wave's 16 FNW columns lie in one 128-row weight block (16 FNW divides
+  // 128 and nw is a multiple of 16 FNW), so its block scales are one row of sw
+  const int nwc = rows > 0 ? nw : 0;
+  const rsrc_t rw = rsrc(W + (int64_t)nwc * K, (int64_t)rows * K);
+  const rsrc_t ra = rsrc(A, (int64_t)M * K);
+  const rsrc_t rsw = rsrc(sw + (int64_t)(nwc >> 7) * KB, (int64_t)KB * 4);
+  const rsrc_t rsa = rsrc(sa, (int64_t)M * KB * 4);
+  uint32_t woff[FNW];
+#pragma unroll
+  for (int f = 0; f < FNW; ++f) woff[f] = (uint32_t)((16 * f + (lane & 15)) * K + q * 16);
+  // group chunk e = threadIdx.x + i NT: block e / CHUNKS, row (e % CHUNKS) >> 3,
+  // 16-byte column e & 7
+  uint32_t aoff[AG];
+  int apos[AG];
+#pragma unroll
+  for (int i = 0; i < AG; ++i) {
+    const int e = threadIdx.x + i * NT;
+    const int bk = e / CHUNKS, r = (e % CHUNKS) >> 3, col = e & 7;
+    const bool ok = e < G * CHUNKS;
+    aoff[i] = ok ? (uint32_t)(r * K + bk * 128 + col * 16) : kOob;
+    apos[i] = ok ? bk * CHUNKS + r * 8 + (col ^ (r & 7)) : -1;
+  }
+  uint32_t soff[SG];
+  int spos[SG];
+#pragma unroll
+  for (int i = 0; i < SG; ++i) {
+    const int e = threadIdx.x + i * NT;
+    const bool ok = MODE == 0 && e < G * ROWS;
+    soff[i] = ok ? (uint32_t)((e % ROWS) * KB * 4 + (e / ROWS) * 4) : kOob;
+    spos[i] = ok ? e : -1;
+  }
+
+  v4f facc[FNW][MF];
+  v4i iacc[FNW][MF];
+#pragma unroll
+  for (int f = 0; f < FNW; ++f)
+#pragma unroll
+    for (int j = 0; j < MF; ++j) {
+      facc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      iacc[f][j] = (v4i){0, 0, 0, 0};
+    }
+
+  v4i areg[AG];
+  float sreg[SG];
+  auto load_act = [&](int g) {  // group g's activations and block scales into registers
+    const uint32_t ko = g < NG ? (uint32_t)g * G * 128u : kOob;
+    const uint32_t so = g < NG ? (uint32_t)g * G * 4u : kOob;
+#pragma unroll
+    for (int i = 0; i < AG; ++i) areg[i] = bl16(ra, aoff[i] + ko);
+    if (MODE == 0) {
+#pragma unroll
+      for (int i = 0; i < SG; ++i) sreg[i] = blf(rsa, soff[i] + so);
+    }
+  };
+  auto store_act = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AG; ++i)
+      if (apos[i] >= 0) as[buf][apos[i]] = areg[i];
+    if (MODE == 0) {
+#pragma unroll
+      for (int i = 0; i < SG; ++i)
+        if (spos[i] >= 0) ss[buf][spos[i]] = sreg[i];
+    }
+  };
+  v4i wv[G][FNW][2];
+  float swv[G];
+  auto load_w = [&](int P, int kb) {
+    const uint32_t ko = kb < KB ? (uint32_t)kb * 128u : kOob;
+#pragma unroll
+    for (int f = 0; f < FNW; ++f) {
+      wv[P][f][0] = bl16(rw, woff[f] + ko);
+      wv[P][f][1] = bl16(rw, woff[f] + ko + 64);
+    }
+    if (MODE == 0) swv[P] = blf(rsw, kb < KB ? (uint32_t)kb * 4u : kOob);
+  };
+
+  // prologue, issued in the order the loop issues: group 0 staged, then the
+  // weight ring, then group 1
+  load_act(0);
+  store_act(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < G; ++p) {
+    load_w(p, p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_act(1);
+  __builtin_amdgcn_sched_barrier(0);
+  waitcnt<63, 0>();
+  barrier();
+
+  for (int g = 0; g < NG; ++g) {
+    const int buf = g & 1;
+#pragma unroll
+    for (int p = 0; p < G; ++p) {
+      v4i af[MF][2];
+      float saj[MF];
+#pragma unroll
+      for (int j = 0; j < MF; ++j) {
+        const int r = 16 * j + (lane & 15);
+        af[j][0] = as[buf][p * CHUNKS + r * 8 + (q ^ (r & 7))];
+        af[j][1] = as[buf][p * CHUNKS + r * 8 + ((4 + q) ^ (r & 7))];
+        if (MODE == 0) saj[j] = ss[buf][p * ROWS + r];
+      }
+#pragma unroll
+      for (int f = 0; f < FNW; ++f)
+#pragma unroll
+        for (int j = 0; j < MF; ++j) {
+          if (MODE == 0) {
+            v4i pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], af[j][0], (v4i){0, 0, 0, 0}, 0, 0, 0);
+            pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], af[j][1], pp, 0, 0, 0);
+            const float s = __fmul_rn(saj[j], swv[p]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(s, (float)pp[r], facc[f][j][r]);
+          } else {
+            iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], af[j][0], iacc[f][j], 0, 0, 0);
+            iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], af[j][1], iacc[f][j], 0, 0, 0);
+          }
+        }
+      load_w(p, (g + 1) * G + p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every wave finished reading buffer buf ^ 1 (group g - 1) before the
+    // previous barrier, so group g + 1 may overwrite it
+    store_act(buf ^ 1);
+    load_act(g + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    waitcnt<63, 0>();
+    barrier();
+  }
+
   const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int f = 0; f < FNW; ++f) {
-    const int n = n0 + f * 16 + 4 * q;
-    if (n >= N) continue;
+    const int n = nw + 16 * f + 4 * q;
 #pragma unroll
     for (int j = 0; j < MF; ++j) {
-      const int m = j * 16 + (lane & 15);
-      if (m >= M) continue;
-      float o[4];
-      if (MODE == 0) {
-        v4f t = __builtin_bit_cast(v4f, red[0][f][j][lane]);
+      const int m = 16 * j + (lane & 15);
+      if (n < N && m < M) {
+        float o[4];
+        if (MODE == 0) {
 #pragma unroll
-        for (int w = 1; w < SK; ++w) t += __builtin_bit_cast(v4f, red[w][f][j][lane]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = t[r];
-      } else {
-        v4i t = red[0][f][j][lane];
-#pragma unroll
-        for (int w = 1; w < SK; ++w) t += red[w][f][j][lane];
-        if (OUT == OUT_I32) {
+          for (int r = 0; r < 4; ++r) o[r] = facc[f][j][r];
+          store_out4<OUT>(Y, (int64_t)m * N + n, n, N, vec, o);
+        } else if (OUT == OUT_I32) {
           int32_t* y = static_cast<int32_t*>(Y) + (int64_t)m * N + n;
+          if (vec && n + 3 < N) {
+            *reinterpret_cast<v4i*>(y) = iacc[f][j];
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) y[r] = t[r];
-          continue;
-        }
-        const float s_m = sa[m];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = n + r < N ? __fmul_rn((float)t[r], __fmul_rn(s_m, sw[n + r])) : 0.f;
-      }
-      const int64_t idx = (int64_t)m * N + n;
-      if (OUT == OUT_F32) {
-        float* y = static_cast<float*>(Y) + idx;
-        if (vec && n + 3 < N) {
-          *reinterpret_cast<float4*>(y) = make_float4(o[0], o[1], o[2], o[3]);
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) y[r] = iacc[f][j][r];
+          }
         } else {
+          const float s_m = sa[m];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (n + r < N) y[r] = o[r];
-        }
-      } else if (OUT == OUT_BF16) {
-        uint16_t* y = static_cast<uint16_t*>(Y) + idx;
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(o[r]);
-        if (vec && n + 3 < N) {
-          *reinterpret_cast<uint2*>(y) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) y[r] = (uint16_t)h[r];
+            o[r] = n + r < N ? __fmul_rn((float)iacc[f][j][r], __fmul_rn(s_m, sw[n + r])) : 0.f;
+          store_out4<OUT>(Y, (int64_t)m * N + n, n, N, vec, o);
         }
       }
     }
@@ -218,46 +440,39 @@ __device__ __forceinline__ v8h i8x8_to_f16(uint32_t lo, uint32_t hi) {
   const v2h bias = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v2h h = __builtin_bit_cast(v2h, w[i]) - bias;
+    const v2h h = __builtin_bit_cast(v2h, w[i]) - bias;
     r[2 * i] = h[0];
     r[2 * i + 1] = h[1];
   }
   return r;
 }
 
-template <int MF, int FNW, int SK>
+// v_mfma_f32_16x16x32_f16 with W as operand A.  Per 128-wide group a lane
+// loads 32 weight bytes of row n (k = 64 h + 16 q + [0, 16), h = 0, 1) and,
+// for MFMA t = 0..3, the 8 activation halves at k = 64 (t/2) + 16 q + 8 (t%2).
+template <int MF, int FNW, int SK, int PF>
 __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __restrict__ x, const int8_t* __restrict__ W,
                                                           const float* __restrict__ ws, uint16_t* __restrict__ Y, int M,
                                                           int N, int K) {
-  __shared__ v4f red[SK][FNW][MF][64];
+  __shared__ v4f red[SK][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int n0 = blockIdx.x * 16 * FNW;
   const int KB = K >> 7;
 
-  const int8_t* wrow[FNW];
-  const float* srow[FNW][4];
+  const int rows = N - n0 < 16 * FNW ? N - n0 : 16 * FNW;
+  const rsrc_t rw = rsrc(W + (int64_t)n0 * K, (int64_t)rows * K);
+  const rsrc_t rs = rsrc(ws + (int64_t)n0 * KB, (int64_t)rows * KB * 4);
+  const rsrc_t rx = rsrc(x, (int64_t)M * K * 2);
+  uint32_t woff[FNW], soff[FNW], xoff[MF];
 #pragma unroll
   for (int f = 0; f < FNW; ++f) {
-    int n = n0 + f * 16 + (lane & 15);
-    n = n < N ? n : N - 1;
-    wrow[f] = W + (int64_t)n * K + q * 16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int no = n0 + f * 16 + 4 * q + r;
-      no = no < N ? no : N - 1;
-      srow[f][r] = ws + (int64_t)no * KB;
-    }
+    woff[f] = (uint32_t)((f * 16 + (lane & 15)) * K + q * 16);
+    soff[f] = (uint32_t)((f * 16 + 4 * q) * KB * 4);
   }
-  const uint16_t* xrow[MF];
-  bool xval[MF];
 #pragma unroll
-  for (int j = 0; j < MF; ++j) {
-    int m = j * 16 + (lane & 15);
-    xval[j] = m < M;
-    xrow[j] = x + (int64_t)(m < M ? m : M - 1) * K + q * 16;
-  }
+  for (int j = 0; j < MF; ++j) xoff[j] = (uint32_t)(((j * 16 + (lane & 15)) * K + q * 16) * 2);
 
   v4f facc[FNW][MF];
 #pragma unroll
@@ -265,67 +480,210 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < MF; ++j) facc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  for (int g = wave; g < KB; g += SK) {
-    // weights: two 16-byte loads per fragment (k = 64 h + 16 q + [0, 16))
-    v4i wv[FNW][2];
+  v4i wv[PF][FNW][2];
+  v8h xv[PF][MF][4];
+  float sv[PF][FNW][4];
+  auto load = [&](int P, int g) {
+    const uint32_t ko = g < KB ? (uint32_t)g * 128u : kOob;
+    const uint32_t so = g < KB ? (uint32_t)g * 4u : kOob;
 #pragma unroll
     for (int f = 0; f < FNW; ++f) {
-      wv[f][0] = ld16(wrow[f] + g * 128);
-      wv[f][1] = ld16(wrow[f] + g * 128 + 64);
+      wv[P][f][0] = bl16(rw, woff[f] + ko);
+      wv[P][f][1] = bl16(rw, woff[f] + ko + 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[P][f][r] = blf(rs, soff[f] + r * KB * 4 + so);
     }
-    // activations: 8 halves per MFMA at k = 64 (t/2) + 16 q + 8 (t%2) + [0, 8)
-    v8h xv[MF][4];
 #pragma unroll
     for (int j = 0; j < MF; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v8h v = *reinterpret_cast<const v8h*>(xrow[j] + g * 128 + (t >> 1) * 64 + (t & 1) * 8);
-        xv[j][t] = xval[j] ? v : (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < 4; ++t)
+        xv[P][j][t] = __builtin_bit_cast(v8h, bl16(rx, xoff[j] + 2 * ko + (t >> 1) * 128 + (t & 1) * 16));
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    load(p, wave + p * SK);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nb = (KB - wave + SK - 1) / SK;
+  const int iters = (nb + PF - 1) / PF;
+  for (int it = 0; it < iters; ++it) {
+    const int g0 = wave + it * SK * PF;
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+#pragma unroll
+      for (int f = 0; f < FNW; ++f) {
+        v8h wh[4];
+        wh[0] = i8x8_to_f16(wv[p][f][0][0], wv[p][f][0][1]);
+        wh[1] = i8x8_to_f16(wv[p][f][0][2], wv[p][f][0][3]);
+        wh[2] = i8x8_to_f16(wv[p][f][1][0], wv[p][f][1][1]);
+        wh[3] = i8x8_to_f16(wv[p][f][1][2], wv[p][f][1][3]);
+#pragma unroll
+        for (int j = 0; j < MF; ++j) {
+          v4f pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) pp = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[t], xv[p][j][t], pp, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(sv[p][f][r], pp[r], facc[f][j][r]);
+        }
       }
-    float s[FNW][4];
-#pragma unroll
-    for (int f = 0; f < FNW; ++f)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[f][r] = srow[f][r][g];
-#pragma unroll
-    for (int f = 0; f < FNW; ++f) {
-      v8h wh[4];
-      wh[0] = i8x8_to_f16(wv[f][0][0], wv[f][0][1]);
-      wh[1] = i8x8_to_f16(wv[f][0][2], wv[f][0][3]);
-      wh[2] = i8x8_to_f16(wv[f][1][0], wv[f][1][1]);
-      wh[3] = i8x8_to_f16(wv[f][1][2], wv[f][1][3]);
-#pragma unroll
-      for (int j = 0; j < MF; ++j) {
-        v4f p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) p = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[t], xv[j][t], p, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(s[f][r], p[r], facc[f][j][r]);
-      }
+      load(p, g0 + p * SK + SK * PF);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
+  const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int f = 0; f < FNW; ++f)
 #pragma unroll
-    for (int j = 0; j < MF; ++j) red[wave][f][j][lane] = facc[f][j];
-  __syncthreads();
-  if (wave != 0) return;
-  const bool vec = (N & 3) == 0;
-#pragma unroll
-  for (int f = 0; f < FNW; ++f) {
-    const int n = n0 + f * 16 + 4 * q;
-    if (n >= N) continue;
-#pragma unroll
     for (int j = 0; j < MF; ++j) {
-      const int m = j * 16 + (lane & 15);
-      if (m >= M) continue;
-      v4f t = red[0][f][j][lane];
+      red[wave][lane] = facc[f][j];
+      __syncthreads();
+      if (wave == ((f * MF + j) % SK)) {
+        const int n = n0 + f * 16 + 4 * q;
+        const int m = j * 16 + (lane & 15);
+        if (n < N && m < M) {
+          v4f t = red[0][lane];
 #pragma unroll
-      for (int w = 1; w < SK; ++w) t += red[w][f][j][lane];
+          for (int w = 1; w < SK; ++w) t += red[w][lane];
+          uint16_t h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = __builtin_bit_cast(uint16_t, (_Float16)t[r]);
+          uint16_t* y = Y + (int64_t)m * N + n;
+          if (vec && n + 3 < N) {
+            *reinterpret_cast<uint2*>(y) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) y[r] = h[r];
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// W8A16 with shared activations: the organisation of k_decode_shared (NWV
+// waves of 16 columns walking the same K blocks, activations staged per
+// workgroup in groups of G K blocks, weights through a G-deep register ring)
+// with the fragment layout of k_decode_w8a16.  A staged row holds 128 fp16
+// values (256 bytes, 16 chunks of 16 bytes); chunk c of row r is stored at
+// c ^ (r & 15).
+template <int MF, int NWV, int G>
+__global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __restrict__ x,
+                                                           const int8_t* __restrict__ W,
+                                                           const float* __restrict__ ws, uint16_t* __restrict__ Y,
+                                                           int M, int N, int K) {
+  constexpr int ROWS = 16 * MF;
+  constexpr int CHUNKS = ROWS * 16;
+  constexpr int NT = 64 * NWV;
+  constexpr int AG = (G * CHUNKS + NT - 1) / NT;
+  __shared__ v4i xs[2][G * CHUNKS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4;
+  const int nw = blockIdx.x * 16 * NWV + 16 * wave;
+  const int KB = K >> 7;
+  const int NG = (KB + G - 1) / G;
+  int rows = N - nw;
+  rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
+  const int nwc = rows > 0 ? nw : 0;
+
+  const rsrc_t rw = rsrc(W + (int64_t)nwc * K, (int64_t)rows * K);
+  const rsrc_t rs = rsrc(ws + (int64_t)nwc * KB, (int64_t)rows * KB * 4);
+  const rsrc_t rx = rsrc(x, (int64_t)M * K * 2);
+  const uint32_t woff = (uint32_t)((lane & 15) * K + q * 16);
+  const uint32_t soff = (uint32_t)(4 * q * KB * 4);
+  uint32_t xoff[AG];
+  int xpos[AG];
+#pragma unroll
+  for (int i = 0; i < AG; ++i) {
+    const int e = threadIdx.x + i * NT;
+    const int bk = e / CHUNKS, r = (e % CHUNKS) >> 4, col = e & 15;
+    const bool ok = e < G * CHUNKS;
+    xoff[i] = ok ? (uint32_t)(r * K * 2 + bk * 256 + col * 16) : kOob;
+    xpos[i] = ok ? bk * CHUNKS + r * 16 + (col ^ (r & 15)) : -1;
+  }
+
+  v4f facc[MF];
+#pragma unroll
+  for (int j = 0; j < MF; ++j) facc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  v4i xreg[AG];
+  auto load_act = [&](int g) {
+    const uint32_t ko = g < NG ? (uint32_t)g * G * 256u : kOob;
+#pragma unroll
+    for (int i = 0; i < AG; ++i) xreg[i] = bl16(rx, xoff[i] + ko);
+  };
+  auto store_act = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AG; ++i)
+      if (xpos[i] >= 0) xs[buf][xpos[i]] = xreg[i];
+  };
+  v4i wv[G][2];
+  float sv[G][4];
+  auto load_w = [&](int P, int kb) {
+    const uint32_t ko = kb < KB ? (uint32_t)kb * 128u : kOob;
+    const uint32_t so = kb < KB ? (uint32_t)kb * 4u : kOob;
+    wv[P][0] = bl16(rw, woff + ko);
+    wv[P][1] = bl16(rw, woff + ko + 64);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[P][r] = blf(rs, soff + r * KB * 4 + so);
+  };
+
+  load_act(0);
+  store_act(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < G; ++p) {
+    load_w(p, p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_act(1);
+  __builtin_amdgcn_sched_barrier(0);
+  waitcnt<63, 0>();
+  barrier();
+
+  for (int g = 0; g < NG; ++g) {
+    const int buf = g & 1;
+#pragma unroll
+    for (int p = 0; p < G; ++p) {
+      v8h wh[4];
+      wh[0] = i8x8_to_f16(wv[p][0][0], wv[p][0][1]);
+      wh[1] = i8x8_to_f16(wv[p][0][2], wv[p][0][3]);
+      wh[2] = i8x8_to_f16(wv[p][1][0], wv[p][1][1]);
+      wh[3] = i8x8_to_f16(wv[p][1][2], wv[p][1][3]);
+#pragma unroll
+      for (int j = 0; j < MF; ++j) {
+        const int r = 16 * j + (lane & 15);
+        v4f pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int c = 8 * (t >> 1) + 2 * q + (t & 1);
+          const v8h xv = __builtin_bit_cast(v8h, xs[buf][p * CHUNKS + r * 16 + (c ^ (r & 15))]);
+          pp = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[t], xv, pp, 0, 0, 0);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) facc[j][rr] = __builtin_fmaf(sv[p][rr], pp[rr], facc[j][rr]);
+      }
+      load_w(p, (g + 1) * G + p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    store_act(buf ^ 1);
+    load_act(g + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    waitcnt<63, 0>();
+    barrier();
+  }
+
+  const bool vec = (N & 3) == 0;
+  const int n = nw + 4 * q;
+#pragma unroll
+  for (int j = 0; j < MF; ++j) {
+    const int m = 16 * j + (lane & 15);
+    if (n < N && m < M) {
       uint16_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = __builtin_bit_cast(uint16_t, (_Float16)t[r]);
+      for (int r = 0; r < 4; ++r) h[r] = __builtin_bit_cast(uint16_t, (_Float16)facc[j][r]);
       uint16_t* y = Y + (int64_t)m * N + n;
       if (vec && n + 3 < N) {
         *reinterpret_cast<uint2*>(y) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
@@ -338,22 +696,125 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
   }
 }
 
+// Waves per workgroup: as many as keep the whole grid resident given the
+// variant's occupancy (waves per SIMD its register use allows), at most 8 and
+// no more than there are K blocks.
+inline int pick_sk(int64_t workgroups, int64_t kblocks, int max_sk, int waves_per_simd) {
+  int sk = (int)((int64_t)kSimds * waves_per_simd / (workgroups > 0 ? workgroups : 1));
+  if (sk > max_sk) sk = max_sk;
+  if (sk > kblocks) sk = (int)kblocks;
+  if (sk >= 8) return 8;
+  if (sk >= 4) return 4;
+  if (sk >= 2) return 2;
+  return 1;
+}
+
+template <int MODE, int MF, int FNW, int PF, int OUT>
+hipError_t decode_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
+                         int64_t N, int64_t K, int waves_per_simd, hipStream_t st) {
+  const int64_t wgs = (N + 16 * FNW - 1) / (16 * FNW);
+  const int sk = pick_sk(wgs, K >> 7, 8, waves_per_simd);
+  const dim3 g((unsigned)wgs);
+  const int m = (int)M, n = (int)N, k = (int)K;
+  switch (sk) {
+    case 8: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 8, PF, OUT>), g, dim3(512), 0, st, A, sa, W, sw, Y, m, n, k); break;
+    case 4: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 4, PF, OUT>), g, dim3(256), 0, st, A, sa, W, sw, Y, m, n, k); break;
+    case 2: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 2, PF, OUT>), g, dim3(128), 0, st, A, sa, W, sw, Y, m, n, k); break;
+    default: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 1, PF, OUT>), g, dim3(64), 0, st, A, sa, W, sw, Y, m, n, k); break;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE, int MF, int NWV, int OUT>
+hipError_t shared_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
+                         int64_t N, int64_t K, hipStream_t st) {
+  const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)));
+  hipLaunchKernelGGL((k_decode_shared<MODE, MF, NWV, 2, OUT>), g, dim3(64 * NWV), 0, st, A, sa, W, sw, Y, (int)M,
+                     (int)N, (int)K);
+  return hipGetLastError();
+}
+
+template <int MODE, int MF, int OUT>
+hipError_t shared_width(int nwv, const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st) {
+  switch (nwv) {
+    case 3: return shared_launch<MODE, MF, 3, OUT>(A, sa, W, sw, Y, M, N, K, st);
+    case 4: return shared_launch<MODE, MF, 4, OUT>(A, sa, W, sw, Y, M, N, K, st);
+    case 6: return shared_launch<MODE, MF, 6, OUT>(A, sa, W, sw, Y, M, N, K, st);
+    case 8: return shared_launch<MODE, MF, 8, OUT>(A, sa, W, sw, Y, M, N, K, st);
+    default: return shared_launch<MODE, MF, 9, OUT>(A, sa, W, sw, Y, M, N, K, st);
+  }
+}
+
+// Workgroup width (waves of 16 columns) for the shared-activation kernel:
+// the weight stream runs at the pace of the most loaded CU, so pick the width
+// whose grid splits most evenly over the CUs (ties go to the wider one, which
+// loads the activations fewer times).  0: no width splits evenly enough.
+inline int pick_shared_width(int64_t N) {
+  static const int widths[] = {9, 8, 6, 4, 3};
+  const int64_t frags = (N + 15) / 16;
+  int best = 0;
+  double best_eff = 0.85;
+  for (int w : widths) {
+    const int64_t wgs = (frags + w - 1) / w;
+    const int64_t per_cu = (wgs + kCUs - 1) / kCUs;
+    const double eff = (double)frags / (double)(kCUs * per_cu * w);
+    if (eff > best_eff + 0.02) {
+      best = w;
+      best_eff = eff;
+    }
+  }
+  return best;
+}
+
 template <int MODE, int OUT>
 hipError_t decode_dispatch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
                            int64_t N, int64_t K, hipStream_t st) {
-  constexpr int SK = 4;
-  const int m = (int)M, n = (int)N, k = (int)K;
-  if (M <= 16) {
-    dim3 g((unsigned)((N + 15) / 16));
-    hipLaunchKernelGGL((k_decode_w8a8<MODE, 1, 1, SK, OUT>), g, dim3(64 * SK), 0, st, A, sa, W, sw, Y, m, n, k);
-  } else if (M <= 32) {
-    dim3 g((unsigned)((N + 31) / 32));
-    hipLaunchKernelGGL((k_decode_w8a8<MODE, 2, 2, SK, OUT>), g, dim3(64 * SK), 0, st, A, sa, W, sw, Y, m, n, k);
-  } else {
-    dim3 g((unsigned)((N + 63) / 64));
-    hipLaunchKernelGGL((k_decode_w8a8<MODE, 4, 4, SK, OUT>), g, dim3(64 * SK), 0, st, A, sa, W, sw, Y, m, n, k);
+  const int nwv = pick_shared_width(N);
+  if (nwv > 0) {
+    if (M <= 16) return shared_width<MODE, 1, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
+    if (M <= 32) return shared_width<MODE, 2, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
+    return shared_width<MODE, 4, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
+  }
+  if (M <= 16) return decode_launch<MODE, 1, 1, 4, OUT>(A, sa, W, sw, Y, M, N, K, 3, st);
+  if (M <= 32) return decode_launch<MODE, 2, 2, 2, OUT>(A, sa, W, sw, Y, M, N, K, 2, st);
+  return decode_launch<MODE, 4, 2, 2, OUT>(A, sa, W, sw, Y, M, N, K, 2, st);
+}
+
+template <int MF, int FNW, int PF>
+hipError_t w8a16_launch(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M, int64_t N, int64_t K,
+                        int waves_per_simd, hipStream_t st) {
+  const int64_t wgs = (N + 16 * FNW - 1) / (16 * FNW);
+  const int sk = pick_sk(wgs, K >> 7, 8, waves_per_simd);
+  const dim3 g((unsigned)wgs);
+  const int n = (int)N, k = (int)K;
+  switch (sk) {
+    case 8: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 8, PF>), g, dim3(512), 0, st, x, W, s, Y, M, n, k); break;
+    case 4: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 4, PF>), g, dim3(256), 0, st, x, W, s, Y, M, n, k); break;
+    case 2: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 2, PF>), g, dim3(128), 0, st, x, W, s, Y, M, n, k); break;
+    default: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 1, PF>), g, dim3(64), 0, st, x, W, s, Y, M, n, k); break;
   }
   return hipGetLastError();
+}
+
+template <int MF, int NWV>
+hipError_t w8a16_shared_launch(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M, int64_t N,
+                               int64_t K, hipStream_t st) {
+  const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)));
+  hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2>), g, dim3(64 * NWV), 0, st, x, W, s, Y, M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+template <int MF>
+hipError_t w8a16_shared_width(int nwv, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M,
+                              int64_t N, int64_t K, hipStream_t st) {
+  switch (nwv) {
+    case 3: return w8a16_shared_launch<MF, 3>(x, W, s, Y, M, N, K, st);
+    case 4: return w8a16_shared_launch<MF, 4>(x, W, s, Y, M, N, K, st);
+    case 6: return w8a16_shared_launch<MF, 6>(x, W, s, Y, M, N, K, st);
+    case 8: return w8a16_shared_launch<MF, 8>(x, W, s, Y, M, N, K, st);
+    default: return w8a16_shared_launch<MF, 9>(x, W, s, Y, M, N, K, st);
+  }
 }
 
 }  // namespace
@@ -375,26 +836,30 @@ hipError_t launch_gemm_channel_decode(const int8_t* A, const float* sa, const in
 
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
                              int64_t K, hipStream_t st) {
-  constexpr int SK = 4;
-  const int m = (int)M, n = (int)N, k = (int)K;
+  const int nwv = pick_shared_width(N);
   // Larger M runs as repeated 64-row slices.
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int mm = (int)(M - m0 < 64 ? M - m0 : 64);
     const uint16_t* xs = x + m0 * K;
     uint16_t* ys = Y + m0 * N;
-    if (mm <= 16) {
-      hipLaunchKernelGGL((k_decode_w8a16<1, 1, SK>), dim3((unsigned)((N + 15) / 16)), dim3(64 * SK), 0, st, xs, W, s,
-                         ys, mm, n, k);
+    hipError_t e;
+    if (nwv > 0) {
+      if (mm <= 16)
+        e = w8a16_shared_width<1>(nwv, xs, W, s, ys, mm, N, K, st);
+      else if (mm <= 32)
+        e = w8a16_shared_width<2>(nwv, xs, W, s, ys, mm, N, K, st);
+      else
+        e = w8a16_shared_width<4>(nwv, xs, W, s, ys, mm, N, K, st);
+    } else if (mm <= 16) {
+      e = w8a16_launch<1, 1, 4>(xs, W, s, ys, mm, N, K, 3, st);
     } else if (mm <= 32) {
-      hipLaunchKernelGGL((k_decode_w8a16<2, 2, SK>), dim3((unsigned)((N + 31) / 32)), dim3(64 * SK), 0, st, xs, W, s,
-                         ys, mm, n, k);
+      e = w8a16_launch<2, 1, 2>(xs, W, s, ys, mm, N, K, 2, st);
     } else {
-      hipLaunchKernelGGL((k_decode_w8a16<4, 4, SK>), dim3((unsigned)((N + 63) / 64)), dim3(64 * SK), 0, st, xs, W, s,
-                         ys, mm, n, k);
+      e = w8a16_launch<4, 1, 1>(xs, W, s, ys, mm, N, K, 2, st);
     }
-    (void)m;
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace w8
