@@ -160,17 +160,56 @@ def test_w8a16_wide(M):
     assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
 
 
-def test_grouped_moe_gemm_with_empty_experts():
-    E, T, topk, K, N = 12, 200, 2, 512, 384
+# 2048 x 8192 is 256 output tiles of 256 x 256: enough to fill the CUs, so
+# the tile kernels run unsplit over K (the small shapes above, with a handful
+# of tiles, run split over K with a reduction of the slices).
+def test_tile_gemms_full_grid_unsplit():
+    M, N, K = 2048, 8192, 256
+    qa, sa, qw, sw = _inputs(M, N, K, seed=11, scheme="block")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    _, y64, y32 = gemm.gemm_block(qa, sa, qw, sw)
+    yf = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    assert gemm.normwise_rel_err(_np(yf), y32) <= 1e-5
+    yb = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+    qa, sa, qw, sw = _inputs(M, N, K, seed=12, scheme="channel")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    ACC, _, y32 = gemm.gemm_channel(qa, sa, qw, sw)
+    assert np.array_equal(_np(w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)), ACC)
+    yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
+    assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
+    yb = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+
+
+# Grouped (MoE) cases: (experts, tokens, top-k, K, N, experts given no
+# tokens, expert made hot).  Few rows per expert run the weight-streaming
+# kernel over 128-row expert tiles (the hot expert spans several tiles; 300
+# experts is more than the tile lookup's 64 lanes x 4); many rows per expert
+# run the LDS-tiled kernel.  N = 400 leaves a ragged last weight block.
+GROUPED_CASES = [
+    (12, 200, 2, 512, 384, (5, 7), None),
+    (40, 1024, 4, 640, 400, (), 3),
+    (300, 256, 8, 256, 256, (0, 299), None),
+    (4, 1024, 2, 512, 400, (), None),
+]
+
+
+@pytest.mark.parametrize("E,T,topk,K,N,empty,hot", GROUPED_CASES)
+def test_grouped_moe_gemm(E, T, topk, K, N, empty, hot):
     lg = synth.router_logits(T, E, seed=4).numpy()
-    lg[:, 5] = -100.0                                 # expert 5 gets no tokens
-    lg[:, 7] = -100.0
+    for e in empty:
+        lg[:, e] = -100.0
+    if hot is not None:
+        lg[:, hot] += 3.0
     rows, exps, offs = routing.topk_route(lg, topk)
-    assert offs[6] == offs[5] and offs[8] == offs[7]
+    for e in empty:
+        assert offs[e + 1] == offs[e]
     x = synth.to_numpy(synth.activations(T, K, seed=8))
     qa, sa = quant.quant_act_group(x[rows])
+    NB = (N + 127) // 128
     qw = np.empty((E, N, K), np.int8)
-    sw = np.empty((E, 3, K // 128), np.float32)
+    sw = np.empty((E, NB, K // 128), np.float32)
     for e in range(E):
         qw[e], sw[e] = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=100 + e)))
     y64, y32 = gemm.gemm_block_grouped(qa, sa, qw, sw, offs)
@@ -185,6 +224,18 @@ def test_grouped_moe_gemm_with_empty_experts():
             assert gemm.normwise_rel_err(yn[r0:r1], y64[r0:r1]) <= TOL64
     yb = w8.gemm_w8a8_block_grouped(A, SA, W, SW, OFF, out_dtype=torch.bfloat16)
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(y))
+
+
+@pytest.mark.parametrize("N", [12280, 36856])
+@pytest.mark.parametrize("M", [80, 128])
+def test_channel_up_to_128_rows_wide(M, N):
+    K = 640
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M + N + 7, scheme="channel")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    ACC, _, y32 = gemm.gemm_channel(qa, sa, qw, sw)
+    assert np.array_equal(_np(w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)), ACC)
+    yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
+    assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
 
 
 def test_gemms_are_deterministic():

@@ -19,6 +19,7 @@
 #include "common.h"
 #include "launch.h"
 #include "pipeline.h"
+#include "grouped.h"
 
 namespace w8 {
 namespace {
@@ -28,6 +29,9 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 // SIMDs per GPU the dispatchers size grids against (256 CUs x 4).
 constexpr int kSimds = 256 * 4;
 constexpr int kCUs = 256;
+// Mode of k_decode_shared beside 0 (block-wise) and 1 (channel-wise):
+// block-wise over experts' row tiles.
+constexpr int MODE_GROUPED_SH = 2;
 
 // Store 4 consecutive outputs of row m (n multiple of 4).
 template <int OUT>
@@ -67,8 +71,15 @@ __device__ __forceinline__ void store_out4(void* Y, int64_t idx, int n, int N, b
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOob = 0x40000000u;
 
+// Base and size are workgroup-uniform; readfirstlane states it, so the
+// descriptor stays in scalar registers (a descriptor the compiler cannot
+// prove uniform gets a loop around every load).
 __device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), 0, n, 0x00020000);
 }
 __device__ __forceinline__ v4i bl16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -235,29 +246,47 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restric
 // group g + 2 is loaded; one barrier per group.  Stage layout: G blocks of
 // 16 MF rows x 128 bytes, row r's 16-byte chunk c stored at c ^ (r & 7), so
 // fragment reads are conflict-free.  Weights stream straight into registers
-// through a G-deep ring.  No cross-wave reduction: every wave covers all of K
-// for its columns.  The dispatcher sizes workgroups so that the grid splits
-// evenly over the CUs (the weight stream runs at the pace of the most loaded
-// CU).
-template <int MODE, int MF, int NWV, int G, int OUT>
+// through a PF-deep ring (PF a multiple of G).  No cross-wave reduction: every
+// wave covers all of K for its columns.  The dispatcher sizes workgroups so
+// that the grid splits evenly over the CUs (the weight stream runs at the pace
+// of the most loaded CU).
+template <int MODE, int MF, int NWV, int G, int PF, int OUT>
 __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                         const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                        void* __restrict__ Y, int M, int N, int K) {
+                                                        const int32_t* __restrict__ offsets, void* __restrict__ Y,
+                                                        int M, int N, int K, int E, int TN) {
   constexpr int FNW = 1;
   constexpr int ROWS = 16 * MF;                                  // activation rows per block
   constexpr int CHUNKS = ROWS * 8;                               // 16-byte chunks per block
   constexpr int NT = 64 * NWV;                                   // threads
   constexpr int AG = (G * CHUNKS + NT - 1) / NT;                 // chunks per thread per group
   constexpr int SG = (G * ROWS + NT - 1) / NT;                   // block scales per thread per group
+  constexpr int SMODE = MODE == MODE_GROUPED_SH ? 0 : MODE;      // arithmetic: 0 block-wise, 1 channel-wise
   __shared__ v4i as[2][G * CHUNKS];
   __shared__ float ss[2][G * ROWS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
-  const int n0 = blockIdx.x * 16 * FNW * NWV;
-  const int nw = n0 + 16 * FNW * wave;
   const int KB = K >> 7;
   const int NG = (KB + G - 1) / G;
+  int cg = blockIdx.x;
+  if (MODE == MODE_GROUPED_SH) {
+    // workgroup = (128-row tile of one expert, column group); rows of the
+    // tile are rows r0 .. r1 - 1 of the permuted activations and outputs
+    const int t = blockIdx.x / TN;
+    cg = blockIdx.x - t * TN;
+    const ExpertTile et = group_tile<ROWS>(offsets, E, M, t);
+    if (et.e < 0) return;
+    const int NB = (N + 127) >> 7;
+    A += (int64_t)et.r0 * K;
+    sa += (int64_t)et.r0 * KB;
+    Y = static_cast<void*>(static_cast<char*>(Y) + (int64_t)et.r0 * N * (OUT == OUT_BF16 ? 2 : 4));
+    W += (int64_t)et.e * N * K;
+    sw += (int64_t)et.e * NB * KB;
+    M = et.r1 - et.r0;
+  }
+  const int n0 = cg * 16 * FNW * NWV;
+  const int nw = n0 + 16 * FNW * wave;
   int rows = N - nw;
   rows = rows < 0 ? 0 : (rows > 16 * FNW ? 16 * FNW : rows);
 
@@ -288,7 +317,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
 #pragma unroll
   for (int i = 0; i < SG; ++i) {
     const int e = threadIdx.x + i * NT;
-    const bool ok = MODE == 0 && e < G * ROWS;
+    const bool ok = SMODE == 0 && e < G * ROWS;
     soff[i] = ok ? (uint32_t)((e % ROWS) * KB * 4 + (e / ROWS) * 4) : kOob;
     spos[i] = ok ? e : -1;
   }
@@ -310,7 +339,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
     const uint32_t so = g < NG ? (uint32_t)g * G * 4u : kOob;
 #pragma unroll
     for (int i = 0; i < AG; ++i) areg[i] = bl16(ra, aoff[i] + ko);
-    if (MODE == 0) {
+    if (SMODE == 0) {
 #pragma unroll
       for (int i = 0; i < SG; ++i) sreg[i] = blf(rsa, soff[i] + so);
     }
@@ -319,14 +348,14 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
 #pragma unroll
     for (int i = 0; i < AG; ++i)
       if (apos[i] >= 0) as[buf][apos[i]] = areg[i];
-    if (MODE == 0) {
+    if (SMODE == 0) {
 #pragma unroll
       for (int i = 0; i < SG; ++i)
         if (spos[i] >= 0) ss[buf][spos[i]] = sreg[i];
     }
   };
-  v4i wv[G][FNW][2];
-  float swv[G];
+  v4i wv[PF][FNW][2];
+  float swv[PF];
   auto load_w = [&](int P, int kb) {
     const uint32_t ko = kb < KB ? (uint32_t)kb * 128u : kOob;
 #pragma unroll
@@ -334,7 +363,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
       wv[P][f][0] = bl16(rw, woff[f] + ko);
       wv[P][f][1] = bl16(rw, woff[f] + ko + 64);
     }
-    if (MODE == 0) swv[P] = blf(rsw, kb < KB ? (uint32_t)kb * 4u : kOob);
+    if (SMODE == 0) swv[P] = blf(rsw, kb < KB ? (uint32_t)kb * 4u : kOob);
   };
 
   // prologue, issued in the order the loop issues: group 0 staged, then the
@@ -343,7 +372,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
   store_act(0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int p = 0; p < G; ++p) {
+  for (int p = 0; p < PF; ++p) {
     load_w(p, p);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -352,44 +381,61 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
   waitcnt<63, 0>();
   barrier();
 
-  for (int g = 0; g < NG; ++g) {
-    const int buf = g & 1;
+  // super-steps of PF K blocks (PF / G activation groups); blocks and groups
+  // past the end read as zero
+  const int iters = (NG * G + PF - 1) / PF;
+  for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int p = 0; p < G; ++p) {
-      v4i af[MF][2];
-      float saj[MF];
+    for (int p = 0; p < PF; ++p) {
+      const int kb = it * PF + p;
+      const int g = it * (PF / G) + p / G;
+      const int buf = g & 1;
+      const int bo = (p % G) * CHUNKS;
+      // row groups in chunks of JC: all of them at once for up to 64 rows,
+      // one at a time beyond (bounds the fragment registers)
+      constexpr int JC = MF <= 4 ? MF : 1;
 #pragma unroll
-      for (int j = 0; j < MF; ++j) {
-        const int r = 16 * j + (lane & 15);
-        af[j][0] = as[buf][p * CHUNKS + r * 8 + (q ^ (r & 7))];
-        af[j][1] = as[buf][p * CHUNKS + r * 8 + ((4 + q) ^ (r & 7))];
-        if (MODE == 0) saj[j] = ss[buf][p * ROWS + r];
-      }
+      for (int j0 = 0; j0 < MF; j0 += JC) {
+        v4i af[JC][2];
+        float saj[JC];
 #pragma unroll
-      for (int f = 0; f < FNW; ++f)
-#pragma unroll
-        for (int j = 0; j < MF; ++j) {
-          if (MODE == 0) {
-            v4i pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], af[j][0], (v4i){0, 0, 0, 0}, 0, 0, 0);
-            pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], af[j][1], pp, 0, 0, 0);
-            const float s = __fmul_rn(saj[j], swv[p]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(s, (float)pp[r], facc[f][j][r]);
-          } else {
-            iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], af[j][0], iacc[f][j], 0, 0, 0);
-            iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], af[j][1], iacc[f][j], 0, 0, 0);
-          }
+        for (int jj = 0; jj < JC; ++jj) {
+          const int r = 16 * (j0 + jj) + (lane & 15);
+          af[jj][0] = as[buf][bo + r * 8 + (q ^ (r & 7))];
+          af[jj][1] = as[buf][bo + r * 8 + ((4 + q) ^ (r & 7))];
+          if (SMODE == 0) saj[jj] = ss[buf][(p % G) * ROWS + r];
         }
-      load_w(p, (g + 1) * G + p);
+#pragma unroll
+        for (int f = 0; f < FNW; ++f)
+#pragma unroll
+          for (int jj = 0; jj < JC; ++jj) {
+            const int j = j0 + jj;
+            if (SMODE == 0) {
+              v4i pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], af[jj][0], (v4i){0, 0, 0, 0}, 0, 0, 0);
+              pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], af[jj][1], pp, 0, 0, 0);
+              const float s = __fmul_rn(saj[jj], swv[p]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(s, (float)pp[r], facc[f][j][r]);
+            } else {
+              iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], af[jj][0], iacc[f][j], 0, 0, 0);
+              iacc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], af[jj][1], iacc[f][j], 0, 0, 0);
+            }
+          }
+        if (JC < MF) __builtin_amdgcn_sched_barrier(0);
+      }
+      load_w(p, kb + PF);
       __builtin_amdgcn_sched_barrier(0);
+      if (p % G == G - 1) {
+        // end of group g: every wave finished reading buffer buf ^ 1
+        // (group g - 1) before the previous barrier, so group g + 1 may
+        // overwrite it
+        store_act(buf ^ 1);
+        load_act(g + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        waitcnt<63, 0>();
+        barrier();
+      }
     }
-    // every wave finished reading buffer buf ^ 1 (group g - 1) before the
-    // previous barrier, so group g + 1 may overwrite it
-    store_act(buf ^ 1);
-    load_act(g + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    waitcnt<63, 0>();
-    barrier();
   }
 
   const bool vec = (N & 3) == 0;
@@ -401,7 +447,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
       const int m = 16 * j + (lane & 15);
       if (n < N && m < M) {
         float o[4];
-        if (MODE == 0) {
+        if (SMODE == 0) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[r] = facc[f][j][r];
           store_out4<OUT>(Y, (int64_t)m * N + n, n, N, vec, o);
@@ -564,11 +610,11 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
 
 // W8A16 with shared activations: the organisation of k_decode_shared (NWV
 // waves of 16 columns walking the same K blocks, activations staged per
-// workgroup in groups of G K blocks, weights through a G-deep register ring)
+// workgroup in groups of G K blocks, weights through a PF-deep register ring)
 // with the fragment layout of k_decode_w8a16.  A staged row holds 128 fp16
 // values (256 bytes, 16 chunks of 16 bytes); chunk c of row r is stored at
 // c ^ (r & 15).
-template <int MF, int NWV, int G>
+template <int MF, int NWV, int G, int PF>
 __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __restrict__ x,
                                                            const int8_t* __restrict__ W,
                                                            const float* __restrict__ ws, uint16_t* __restrict__ Y,
@@ -619,8 +665,8 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
     for (int i = 0; i < AG; ++i)
       if (xpos[i] >= 0) xs[buf][xpos[i]] = xreg[i];
   };
-  v4i wv[G][2];
-  float sv[G][4];
+  v4i wv[PF][2];
+  float sv[PF][4];
   auto load_w = [&](int P, int kb) {
     const uint32_t ko = kb < KB ? (uint32_t)kb * 128u : kOob;
     const uint32_t so = kb < KB ? (uint32_t)kb * 4u : kOob;
@@ -634,7 +680,7 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
   store_act(0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int p = 0; p < G; ++p) {
+  for (int p = 0; p < PF; ++p) {
     load_w(p, p);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -643,10 +689,14 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
   waitcnt<63, 0>();
   barrier();
 
-  for (int g = 0; g < NG; ++g) {
-    const int buf = g & 1;
+  const int iters = (NG * G + PF - 1) / PF;
+  for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int p = 0; p < G; ++p) {
+    for (int p = 0; p < PF; ++p) {
+      const int kb = it * PF + p;
+      const int g = it * (PF / G) + p / G;
+      const int buf = g & 1;
+      const int bo = (p % G) * CHUNKS;
       v8h wh[4];
       wh[0] = i8x8_to_f16(wv[p][0][0], wv[p][0][1]);
       wh[1] = i8x8_to_f16(wv[p][0][2], wv[p][0][3]);
@@ -659,20 +709,22 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int c = 8 * (t >> 1) + 2 * q + (t & 1);
-          const v8h xv = __builtin_bit_cast(v8h, xs[buf][p * CHUNKS + r * 16 + (c ^ (r & 15))]);
+          const v8h xv = __builtin_bit_cast(v8h, xs[buf][bo + r * 16 + (c ^ (r & 15))]);
           pp = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[t], xv, pp, 0, 0, 0);
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) facc[j][rr] = __builtin_fmaf(sv[p][rr], pp[rr], facc[j][rr]);
       }
-      load_w(p, (g + 1) * G + p);
+      load_w(p, kb + PF);
       __builtin_amdgcn_sched_barrier(0);
+      if (p % G == G - 1) {
+        store_act(buf ^ 1);
+        load_act(g + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        waitcnt<63, 0>();
+        barrier();
+      }
     }
-    store_act(buf ^ 1);
-    load_act(g + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    waitcnt<63, 0>();
-    barrier();
   }
 
   const bool vec = (N & 3) == 0;
@@ -725,24 +777,47 @@ hipError_t decode_launch(const int8_t* A, const float* sa, const int8_t* W, cons
   return hipGetLastError();
 }
 
-template <int MODE, int MF, int NWV, int OUT>
+// Weight-ring depth for the shared-activation kernels: a CU needs about
+// 44 KB of weights in flight (its share of the HBM stream times the loaded
+// latency), i.e. 22 K-block slots of 2 KB over its resident waves.
+inline int pick_ring_depth(int64_t N, int nwv) {
+  const int64_t wgs = (N + 16 * nwv - 1) / (16 * nwv);
+  const int64_t waves_per_cu = nwv * ((wgs + kCUs - 1) / kCUs);
+  return waves_per_cu <= 4 ? 8 : (waves_per_cu <= 8 ? 4 : 2);
+}
+
+template <int MODE, int MF, int NWV, int PF, int OUT>
 hipError_t shared_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
                          int64_t N, int64_t K, hipStream_t st) {
   const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)));
-  hipLaunchKernelGGL((k_decode_shared<MODE, MF, NWV, 2, OUT>), g, dim3(64 * NWV), 0, st, A, sa, W, sw, Y, (int)M,
-                     (int)N, (int)K);
+  hipLaunchKernelGGL((k_decode_shared<MODE, MF, NWV, 2, PF, OUT>), g, dim3(64 * NWV), 0, st, A, sa, W, sw, nullptr, Y,
+                     (int)M, (int)N, (int)K, 0, 0);
   return hipGetLastError();
+}
+
+template <int MODE, int MF, int NWV, int OUT>
+hipError_t shared_depth(int pf, const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st) {
+  // (only the pairings the depth rule can produce are instantiated)
+  if constexpr (NWV <= 4) {
+    if (pf == 8) return shared_launch<MODE, MF, NWV, 8, OUT>(A, sa, W, sw, Y, M, N, K, st);
+  }
+  if constexpr (NWV <= 8) {
+    if (pf >= 4) return shared_launch<MODE, MF, NWV, 4, OUT>(A, sa, W, sw, Y, M, N, K, st);
+  }
+  return shared_launch<MODE, MF, NWV, 2, OUT>(A, sa, W, sw, Y, M, N, K, st);
 }
 
 template <int MODE, int MF, int OUT>
 hipError_t shared_width(int nwv, const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
                         int64_t N, int64_t K, hipStream_t st) {
+  const int pf = pick_ring_depth(N, nwv);
   switch (nwv) {
-    case 3: return shared_launch<MODE, MF, 3, OUT>(A, sa, W, sw, Y, M, N, K, st);
-    case 4: return shared_launch<MODE, MF, 4, OUT>(A, sa, W, sw, Y, M, N, K, st);
-    case 6: return shared_launch<MODE, MF, 6, OUT>(A, sa, W, sw, Y, M, N, K, st);
-    case 8: return shared_launch<MODE, MF, 8, OUT>(A, sa, W, sw, Y, M, N, K, st);
-    default: return shared_launch<MODE, MF, 9, OUT>(A, sa, W, sw, Y, M, N, K, st);
+    case 3: return shared_depth<MODE, MF, 3, OUT>(pf, A, sa, W, sw, Y, M, N, K, st);
+    case 4: return shared_depth<MODE, MF, 4, OUT>(pf, A, sa, W, sw, Y, M, N, K, st);
+    case 6: return shared_depth<MODE, MF, 6, OUT>(pf, A, sa, W, sw, Y, M, N, K, st);
+    case 8: return shared_depth<MODE, MF, 8, OUT>(pf, A, sa, W, sw, Y, M, N, K, st);
+    default: return shared_depth<MODE, MF, 9, OUT>(pf, A, sa, W, sw, Y, M, N, K, st);
   }
 }
 
@@ -774,6 +849,9 @@ hipError_t decode_dispatch(const int8_t* A, const float* sa, const int8_t* W, co
   if (nwv > 0) {
     if (M <= 16) return shared_width<MODE, 1, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
     if (M <= 32) return shared_width<MODE, 2, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
+    if constexpr (MODE == 1) {
+      if (M > 64) return shared_width<MODE, 8, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
+    }
     return shared_width<MODE, 4, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
   }
   if (M <= 16) return decode_launch<MODE, 1, 1, 4, OUT>(A, sa, W, sw, Y, M, N, K, 3, st);
@@ -797,27 +875,60 @@ hipError_t w8a16_launch(const uint16_t* x, const int8_t* W, const float* s, uint
   return hipGetLastError();
 }
 
-template <int MF, int NWV>
+template <int MF, int NWV, int PF>
 hipError_t w8a16_shared_launch(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M, int64_t N,
                                int64_t K, hipStream_t st) {
   const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)));
-  hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2>), g, dim3(64 * NWV), 0, st, x, W, s, Y, M, (int)N, (int)K);
+  hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2, PF>), g, dim3(64 * NWV), 0, st, x, W, s, Y, M, (int)N, (int)K);
   return hipGetLastError();
+}
+
+template <int MF, int NWV>
+hipError_t w8a16_shared_depth(int pf, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M,
+                              int64_t N, int64_t K, hipStream_t st) {
+  if constexpr (NWV <= 4) {
+    if (pf == 8) return w8a16_shared_launch<MF, NWV, 8>(x, W, s, Y, M, N, K, st);
+  }
+  if constexpr (NWV <= 8) {
+    if (pf >= 4) return w8a16_shared_launch<MF, NWV, 4>(x, W, s, Y, M, N, K, st);
+  }
+  return w8a16_shared_launch<MF, NWV, 2>(x, W, s, Y, M, N, K, st);
 }
 
 template <int MF>
 hipError_t w8a16_shared_width(int nwv, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M,
                               int64_t N, int64_t K, hipStream_t st) {
+  const int pf = pick_ring_depth(N, nwv);
   switch (nwv) {
-    case 3: return w8a16_shared_launch<MF, 3>(x, W, s, Y, M, N, K, st);
-    case 4: return w8a16_shared_launch<MF, 4>(x, W, s, Y, M, N, K, st);
-    case 6: return w8a16_shared_launch<MF, 6>(x, W, s, Y, M, N, K, st);
-    case 8: return w8a16_shared_launch<MF, 8>(x, W, s, Y, M, N, K, st);
-    default: return w8a16_shared_launch<MF, 9>(x, W, s, Y, M, N, K, st);
+    case 3: return w8a16_shared_depth<MF, 3>(pf, x, W, s, Y, M, N, K, st);
+    case 4: return w8a16_shared_depth<MF, 4>(pf, x, W, s, Y, M, N, K, st);
+    case 6: return w8a16_shared_depth<MF, 6>(pf, x, W, s, Y, M, N, K, st);
+    case 8: return w8a16_shared_depth<MF, 8>(pf, x, W, s, Y, M, N, K, st);
+    default: return w8a16_shared_depth<MF, 9>(pf, x, W, s, Y, M, N, K, st);
   }
 }
 
 }  // namespace
+
+bool decode_path_takes(int64_t M, int64_t N, bool channel) {
+  return M <= 64 || (channel && M <= 128 && pick_shared_width(N) > 0);
+}
+
+hipError_t launch_gemm_block_grouped_shared(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
+                                            const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P,
+                                            int64_t N, int64_t K, hipStream_t st) {
+  constexpr int NWV = 8;
+  const int64_t TN = (N + 16 * NWV - 1) / (16 * NWV);
+  const int64_t TM = (P + 127) / 128 + E;  // upper bound on the experts' 128-row tiles
+  const dim3 g((unsigned)(TM * TN));
+  if (out == OUT_BF16)
+    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 8, NWV, 2, 2, OUT_BF16>), g, dim3(64 * NWV), 0, st, A, sa, W, sw,
+                       offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
+  else
+    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 8, NWV, 2, 2, OUT_F32>), g, dim3(64 * NWV), 0, st, A, sa, W, sw,
+                       offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_block_decode(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                     OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
@@ -843,10 +954,10 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s,
     const uint16_t* xs = x + m0 * K;
     uint16_t* ys = Y + m0 * N;
     hipError_t e;
-    if (nwv > 0) {
-      if (mm <= 16)
-        e = w8a16_shared_width<1>(nwv, xs, W, s, ys, mm, N, K, st);
-      else if (mm <= 32)
+    // up to 16 rows the activations are cheap to reload per wave, and the
+    // split-K kernel (more waves, no barriers) streams faster
+    if (nwv > 0 && mm > 16) {
+      if (mm <= 32)
         e = w8a16_shared_width<2>(nwv, xs, W, s, ys, mm, N, K, st);
       else
         e = w8a16_shared_width<4>(nwv, xs, W, s, ys, mm, N, K, st);

@@ -16,6 +16,9 @@
 // contiguous stores, one activation scale per lane and fragment, and (block
 // scheme) one weight scale per wave, because a wave's 128 columns lie inside
 // one 128-wide N block.
+#include <mutex>
+#include <vector>
+
 #include "launch.h"
 #include "pipeline.h"
 
@@ -99,11 +102,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   const int m0 = tm * kChBM, n0 = tn * kChBN;
   const int mval = M - m0 < kChBM ? M - m0 : kChBM;
   const int nval = N - n0 < kChBN ? N - n0 : kChBN;
-  const v4i ra = make_rsrc(A + (int64_t)m0 * K, (uint32_t)(mval * K));
-  const v4i rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(nval * K));
+  // split-K: slice blockIdx.y of gridDim.y covers K blocks kbs .. kbe - 1 and
+  // writes its raw int32 tile to slice blockIdx.y of Y (M x N each)
+  const int KBt = K >> 7;
+  const int kbs = (int)((int64_t)blockIdx.y * KBt / gridDim.y);
+  const int kbe = (int)((int64_t)(blockIdx.y + 1) * KBt / gridDim.y);
+  Y = static_cast<void*>(static_cast<int32_t*>(Y) + (int64_t)blockIdx.y * M * N);
+  // the slice's first K block is the descriptors' origin; rows past the tile
+  // still fall outside their range
+  const v4i ra = make_rsrc(A + (int64_t)m0 * K + kbs * 128, (uint32_t)(mval * K - kbs * 128));
+  const v4i rw = make_rsrc(W + (int64_t)n0 * K + kbs * 128, (uint32_t)(nval * K - kbs * 128));
   const int voff = wave * 64 * K + dma_lane_off(lane, K);   // wave fills tile rows 64*wave .. +63
   const uint32_t lds0 = lds_addr(smem);
-  const int NK = K >> 7;
+  const int NK = kbe - kbs;
   const int K8 = 8 * K;
   const int lo0 = frag_off(lane & 15, lane >> 4);           // 16x16x64 operand: row l%16, chunk l/16
   const int lo1 = frag_off(lane & 15, 4 + (lane >> 4));
@@ -294,8 +305,14 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     mrows = M - m0 < BM ? M - m0 : BM;
   }
   const int nval = N - n0 < BN ? N - n0 : BN;
-  const v4i ra = make_rsrc(A + (int64_t)m0 * K, (uint32_t)(mrows * K));
-  const v4i rw = make_rsrc(Wx + (int64_t)n0 * K, (uint32_t)(nval * K));
+  // split-K (dequantising mode only): slice blockIdx.y of gridDim.y covers K
+  // blocks kbs .. kbe - 1 and writes its fp32 partial tile to slice
+  // blockIdx.y of Y (M x N each)
+  const int kbs = (int)((int64_t)blockIdx.y * KB / gridDim.y);
+  const int kbe = (int)((int64_t)(blockIdx.y + 1) * KB / gridDim.y);
+  if (MODE == MODE_DEQUANT) Y = static_cast<void*>(static_cast<float*>(Y) + (int64_t)blockIdx.y * M * N);
+  const v4i ra = make_rsrc(A + (int64_t)m0 * K + kbs * 128, (uint32_t)(mrows * K - kbs * 128));
+  const v4i rw = make_rsrc(Wx + (int64_t)n0 * K + kbs * 128, (uint32_t)(nval * K - kbs * 128));
   const int voffA = wave * AI * 8 * K + dma_lane_off(lane, K);
   const int voffW = wave * WI * 8 * K + dma_lane_off(lane, K);
   const uint32_t lds0 = lds_addr(smem);
@@ -307,12 +324,12 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   // this wave's 128 columns lie in one 128-wide N block
   int nbw = (n0 + wn * 128) >> 7;
   nbw = nbw < NB ? nbw : NB - 1;
-  const float* sw_row = swx + (int64_t)nbw * KB;
+  const float* sw_row = swx + (int64_t)nbw * KB + kbs;
   const float* sa_row[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = wm * 64 + j * 32 + (lane & 31);
-    sa_row[j] = sa + (int64_t)(m0 + (r < mrows ? r : mrows - 1)) * KB;
+    sa_row[j] = sa + (int64_t)(m0 + (r < mrows ? r : mrows - 1)) * KB + kbs;
   }
 
   v4f facc[4][2][4];
@@ -335,11 +352,12 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   }
 
   const bool vec = (N & 3) == 0;
+  const int NKs = kbe - kbs;          // K blocks of this slice, numbered from its first
   BK_DMA(0)
-  for (int kb = 0; kb < KB; ++kb) {
+  for (int kb = 0; kb < NKs; ++kb) {
     waitcnt<0, 0>();                  // block kb landed (own loads); own reads of kb-1 done
     barrier();                        // everyone's block kb landed; everyone is past kb-1
-    if (kb + 1 < KB) BK_DMA(kb + 1)   // into the slot kb-1 used
+    if (kb + 1 < NKs) BK_DMA(kb + 1)  // into the slot kb-1 used
     const char* buf = smem + (kb & 1) * STG;
     float s[2];
     if (MODE != MODE_PARTIALS) {
@@ -412,12 +430,146 @@ void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float
                      TN, E);
 }
 
+// ---------------------------------------------------------------- split-K
+// Sum of the S slices' partial tiles, in slice order, then the output.
+// Channel-wise: int32 slices (the sum is exact) and the channel epilogue
+// fp32(fp32(acc) * fp32(sa[m] * sw[n])); block-wise: fp32 slices.  Each
+// thread covers 4 consecutive outputs of one row.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_splitk_sum_i32(const int32_t* __restrict__ ws, int S, int M, int N,
+                                                        const float* __restrict__ sa, const float* __restrict__ sw,
+                                                        void* __restrict__ Y) {
+  const int64_t q4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nq = (N + 3) >> 2;
+  if (q4 >= (int64_t)M * nq) return;
+  const int m = (int)(q4 / nq), n = (int)(q4 - (int64_t)m * nq) * 4;
+  const int64_t idx = (int64_t)m * N + n;
+  const int64_t MN = (int64_t)M * N;
+  v4i a = {0, 0, 0, 0};
+  for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) a[r] += ws[sl * MN + idx + r];
+  const bool vec = (N & 3) == 0;
+  if (OUT == OUT_I32) {
+    store4i(static_cast<int32_t*>(Y) + idx, n, N, vec, a);
+  } else {
+    float o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = n + r < N ? __fmul_rn((float)a[r], __fmul_rn(sa[m], sw[n + r])) : 0.f;
+    store4<OUT>(Y, idx, n, N, vec, o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256) void k_splitk_sum_f32(const float* __restrict__ ws, int S, int M, int N,
+                                                        void* __restrict__ Y) {
+  const int64_t q4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nq = (N + 3) >> 2;
+  if (q4 >= (int64_t)M * nq) return;
+  const int m = (int)(q4 / nq), n = (int)(q4 - (int64_t)m * nq) * 4;
+  const int64_t idx = (int64_t)m * N + n;
+  const int64_t MN = (int64_t)M * N;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) o[r] = __fadd_rn(o[r], ws[sl * MN + idx + r]);
+  store4<OUT>(Y, idx, n, N, (N & 3) == 0, o[0], o[1], o[2], o[3]);
+}
+
+// Number of K slices for a tile grid that leaves CUs idle: the smallest
+// modelled time over S = 1..16, where a slice of KB / S blocks costs one
+// round of workgroups per 256, t_kb microseconds per tile and K block, and
+// splitting adds the slices' partial tiles through HBM (written and read,
+// 8 bytes per output per slice at ~5 TB/s) plus a reduction launch.
+int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us) {
+  int best = 1;
+  double best_t = 1e30;
+  for (int S = 1; S <= 16 && S <= KB; ++S) {
+    const int64_t rounds = (tiles * S + 255) / 256;
+    double t = (double)rounds * ((double)KB / S) * t_kb_us;
+    if (S > 1) t += (double)S * M * N * 8.0 / 5.0e6 + 3.0;
+    if (t < best_t * 0.97) {
+      best_t = t;
+      best = S;
+    }
+  }
+  return best;
+}
+
+// Per-(device, stream) workspace for split-K partial tiles, grown on demand
+// and kept until the process ends.  Calls on one stream are ordered, so they
+// may share it; different streams get different buffers.
+struct Workspace {
+  int dev;
+  hipStream_t st;
+  void* p;
+  size_t bytes;
+};
+std::mutex g_ws_mu;
+std::vector<Workspace> g_ws;
+
+hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (Workspace& w : g_ws) {
+    if (w.dev == dev && w.st == st) {
+      if (w.bytes < bytes) {
+        // the stream's earlier kernels may still read the old buffer
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return e;
+        e = hipFree(w.p);
+        if (e != hipSuccess) return e;
+        w.p = nullptr;
+        w.bytes = 0;
+        e = hipMalloc(&w.p, bytes);
+        if (e != hipSuccess) return e;
+        w.bytes = bytes;
+      }
+      *out = w.p;
+      return hipSuccess;
+    }
+  }
+  void* p = nullptr;
+  e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) return e;
+  g_ws.push_back({dev, st, p, bytes});
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (M <= 64) return launch_gemm_channel_decode(A, sa, W, sw, Y, out, M, N, K, st);
+  if (decode_path_takes(M, N, true)) return launch_gemm_channel_decode(A, sa, W, sw, Y, out, M, N, K, st);
   const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + kChBN - 1) / kChBN);
+  // ~2.2 us per 256 x 256 tile and K block at the measured large-M rate
+  const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, 2.2);
+  if (S > 1) {
+    void* ws = nullptr;
+    hipError_t e = split_workspace(st, (size_t)S * M * N * 4, &ws);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_channel<OUT_I32>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(256), 0, st, A, sa, W,
+                       sw, ws, (int)M, (int)N, (int)K, TM);
+    const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
+    const int32_t* wsi = static_cast<const int32_t*>(ws);
+    switch (out) {
+      case OUT_BF16:
+        hipLaunchKernelGGL((k_splitk_sum_i32<OUT_BF16>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
+        break;
+      case OUT_F32:
+        hipLaunchKernelGGL((k_splitk_sum_i32<OUT_F32>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
+        break;
+      default:
+        hipLaunchKernelGGL((k_splitk_sum_i32<OUT_I32>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
+        break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)(TM * TN)), block(256);
   switch (out) {
     case OUT_BF16:
@@ -435,22 +587,37 @@ hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W
 
 hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                              OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (M <= 64) return launch_gemm_block_decode(A, sa, W, sw, Y, out, M, N, K, st);
+  if (decode_path_takes(M, N, false)) return launch_gemm_block_decode(A, sa, W, sw, Y, out, M, N, K, st);
   const int TN = (int)((N + 255) / 256);
-  if (M <= 128) {
-    const int TM = (int)((M + 127) / 128);
-    dim3 grid((unsigned)(TM * TN));
-    if (out == OUT_BF16)
-      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+  const int BM = M <= 128 ? 128 : 256;
+  const int TM = (int)((M + BM - 1) / BM);
+  // ~3.3 us per 256 x 256 tile and K block at the measured large-M rate
+  const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, BM == 256 ? 3.3 : 1.9);
+  void* dst = Y;
+  if (S > 1) {
+    hipError_t e = split_workspace(st, (size_t)S * M * N * 4, &dst);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(TM * TN), (unsigned)S);
+  const bool f32 = S > 1 || out == OUT_F32;
+  if (BM == 128) {
+    if (f32)
+      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
     else
-      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
   } else {
-    const int TM = (int)((M + 255) / 256);
-    dim3 grid((unsigned)(TM * TN));
-    if (out == OUT_BF16)
-      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 4>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+    if (f32)
+      launch_block_kernel<MODE_DEQUANT, OUT_F32, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
     else
-      launch_block_kernel<MODE_DEQUANT, OUT_F32, 4>(grid, st, A, sa, W, sw, nullptr, Y, (int)M, (int)N, (int)K, TM, TN, 0);
+      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
+  }
+  if (S > 1) {
+    const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
+    const float* wsf = static_cast<const float*>(dst);
+    if (out == OUT_BF16)
+      hipLaunchKernelGGL((k_splitk_sum_f32<OUT_BF16>), rg, dim3(256), 0, st, wsf, S, (int)M, (int)N, Y);
+    else
+      hipLaunchKernelGGL((k_splitk_sum_f32<OUT_F32>), rg, dim3(256), 0, st, wsf, S, (int)M, (int)N, Y);
   }
   return hipGetLastError();
 }
@@ -466,6 +633,10 @@ hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t*
 hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
                                      const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P, int64_t N,
                                      int64_t K, hipStream_t st) {
+  // few rows per expert: the expert weights are streamed once per 128-row
+  // tile, and the weight stream sets the pace
+  if (E > 0 && P <= 256 * E)
+    return launch_gemm_block_grouped_shared(A, sa, W, sw, offsets, Y, out, E, P, N, K, st);
   // upper bound on the number of 128-row m-tiles over all experts
   const int64_t TMmax = (P + 127) / 128 + E;
   const int TN = (int)((N + 255) / 256);

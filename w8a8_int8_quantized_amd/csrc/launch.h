@@ -30,10 +30,18 @@ hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
                              int64_t K, hipStream_t st);
 
-// Small-M (decode) variants, used by the dispatchers above when M is small.
+// Small-M (weight-streaming) variants, used by the dispatchers above for the
+// shapes decode_path_takes accepts: every M <= 64, and channel-wise M <= 128
+// where the grid of the workgroup-shared kernel splits evenly over the CUs.
+bool decode_path_takes(int64_t M, int64_t N, bool channel);
 hipError_t launch_gemm_block_decode(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                     OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm_channel_decode(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                       OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+// Grouped block-wise GEMM over experts' 128-row tiles with weight streaming,
+// for few rows per expert.
+hipError_t launch_gemm_block_grouped_shared(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
+                                            const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P,
+                                            int64_t N, int64_t K, hipStream_t st);
 
 }  // namespace w8
