@@ -164,7 +164,7 @@ def test_w8a16_wide(M):
 # the tile kernels run unsplit over K (the small shapes above, with a handful
 # of tiles, run split over K with a reduction of the slices).
 def test_tile_gemms_full_grid_unsplit():
-    M, N, K = 2048, 8192, 256
+    M, N, K = 2048, 8192, 768
     qa, sa, qw, sw = _inputs(M, N, K, seed=11, scheme="block")
     A, SA, W, SW = _dev(qa, sa, qw, sw)
     _, y64, y32 = gemm.gemm_block(qa, sa, qw, sw)

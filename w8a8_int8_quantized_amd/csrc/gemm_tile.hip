@@ -174,28 +174,93 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   }
 #undef CH_DMA
 #undef CH_RD
-  waitcnt<0, 15>();
+  // every load, and the loop's last (unused) look-ahead read, has landed
+  waitcnt<0, 0>();
 
   const bool vec = (N & 3) == 0;
+  if (OUT == OUT_I32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = m0 + wm * 128 + j * 16 + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+        if (n < N) store4i(static_cast<int32_t*>(Y) + (int64_t)m * N + n, n, N, vec, acc[i][j]);
+      }
+    }
+    return;
+  }
+  // this lane's 8 activation scales and 8 x 4 weight scales, all loads in
+  // flight at once
+  float sam[8], swn[8][4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int m = m0 + wm * 128 + j * 16 + (lane & 15);
-    if (m >= M) continue;
-    const float s_m = OUT == OUT_I32 ? 0.f : sa[m];
+    sam[j] = m < M ? sa[m] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) swn[i][r] = n + r < N ? sw[n + r] : 0.f;
+  }
+  if (OUT == OUT_F32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = m0 + wm * 128 + j * 16 + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+        if (n >= N) continue;
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = __fmul_rn((float)acc[i][j][r], __fmul_rn(sam[j], swn[i][r]));
+        store4<OUT_F32>(Y, (int64_t)m * N + n, n, N, vec, o[0], o[1], o[2], o[3]);
+      }
+    }
+    return;
+  }
+  // bf16: the tile goes through LDS (free now: the barrier below also means
+  // every wave is past its last stage read) so that it leaves in whole rows.
+  // Tile row r holds 256 bf16 (512 bytes); its 16-byte chunk c is stored at
+  // c ^ (r & 15), so the 16 rows a write instruction touches, and the 32
+  // chunks a row read touches, fall in distinct bank groups.
+  barrier();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wm * 128 + j * 16 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
-      if (n >= N) continue;
-      const int64_t idx = (int64_t)m * N + n;
-      if (OUT == OUT_I32) {
-        store4i(static_cast<int32_t*>(Y) + idx, n, N, vec, acc[i][j]);
-      } else {
-        float s4[4];
+      uint32_t h[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s4[r] = n + r < N ? __fmul_rn(s_m, sw[n + r]) : 0.f;
-        store4<OUT>(Y, idx, n, N, vec, __fmul_rn((float)acc[i][j][0], s4[0]), __fmul_rn((float)acc[i][j][1], s4[1]),
-                    __fmul_rn((float)acc[i][j][2], s4[2]), __fmul_rn((float)acc[i][j][3], s4[3]));
-      }
+      for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(__fmul_rn((float)acc[i][j][q], __fmul_rn(sam[j], swn[i][q])));
+      const int chunk = wn * 16 + 2 * i + (lane >> 5);
+      *reinterpret_cast<uint2*>(smem + r * 512 + ((chunk ^ (r & 15)) << 4) + 8 * ((lane >> 4) & 1)) =
+          make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+  }
+  waitcnt<63, 0>();
+  barrier();
+  // wave w stores tile rows 64 w .. 64 w + 63, two rows per instruction;
+  // lane: row half lane >> 5, columns 8 (lane & 31) .. + 7
+  const int cl = lane & 31;
+  const int n = n0 + 8 * cl;
+  const bool vec8 = (N & 7) == 0 && n + 7 < N;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int r = wave * 64 + 2 * it + (lane >> 5);
+    const int m = m0 + r;
+    const v4i v = *reinterpret_cast<const v4i*>(smem + r * 512 + ((cl ^ (r & 15)) << 4));
+    if (m >= M || n >= N) continue;
+    uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)m * N + n;
+    if (vec8) {
+      *reinterpret_cast<v4i*>(y) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) y[e] = (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1)));
     }
   }
 }
@@ -406,6 +471,49 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   waitcnt<0, 15>();
 
   if (MODE == MODE_PARTIALS) return;
+  if (OUT == OUT_BF16) {
+    // the bf16 tile goes through LDS (row r of 256 bf16, 16-byte chunk c at
+    // c ^ (r & 15)) so that it leaves in whole rows; the barrier also means
+    // every wave is past its last stage read
+    waitcnt<0, 0>();
+    barrier();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = wm * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(facc[i][j][g][q]);
+          const int chunk = wn * 16 + i * 4 + g;
+          *reinterpret_cast<uint2*>(smem + r * 512 + ((chunk ^ (r & 15)) << 4) + 8 * (lane >> 5)) =
+              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        }
+    }
+    waitcnt<63, 0>();
+    barrier();
+    // wave w stores tile rows 32 w .. 32 w + 31, two rows per instruction
+    const int cl = lane & 31;
+    const int n = n0 + 8 * cl;
+    const bool vec8 = (N & 7) == 0 && n + 7 < N;
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int r = wave * 32 + 2 * it + (lane >> 5);
+      const v4i v = *reinterpret_cast<const v4i*>(smem + r * 512 + ((cl ^ (r & 15)) << 4));
+      if (r >= mrows || n >= N) continue;
+      uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)(m0 + r) * N + n;
+      if (vec8) {
+        *reinterpret_cast<v4i*>(y) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) y[e] = (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ml = wm * 64 + j * 32 + (lane & 31);
