@@ -39,7 +39,7 @@ DOWN = (18432, 7168)
 # traffic of the dominant kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
 # scaled by the same counters' reading for a copy kernel of known size; None
 # until counters have been taken for the current kernel.
-TRAFFIC_GATE_UP_BYTES = 2.682e9   # rocprofv3 FETCH_SIZE x2.000 + WRITE_SIZE x1.000 (copy-calibrated), per launch
+TRAFFIC_GATE_UP_BYTES = 2.694e9   # rocprofv3 FETCH_SIZE x2.000 + WRITE_SIZE x1.000 (copy-calibrated), per launch
 
 
 def parse():
@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rows-reps", type=int, default=20)
+    ap.add_argument("--rows-only", default="",
+                    help="comma list of row groups to run: quant,tile,decode,w8a16,moe (default all)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the reference kernel of known "
                          "size for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -153,117 +155,127 @@ def rows(args):
                 "mfma_frac": round(ops / ms / 1e9 / PEAK_INT8_TOPS, 3),
                 "GBps": round(byts / ms / 1e6, 1), "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
 
-    # --- quantisers at M = 4096, K = 7168 (bytes: 2 in + 1 out + scales)
-    x = synth.activations(4096, 7168, seed=2, device=dev)
-    ms = time_calls(lambda i: w8.quant_act_group(x), 1, R)
-    b = 4096 * 7168 * 3 + 4096 * 56 * 4
-    out["quant_act_group_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
-                                        "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
-    ms = time_calls(lambda i: w8.quant_act_token(x), 1, R)
-    b = 4096 * 7168 * 3 + 4096 * 4
-    out["quant_act_token_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
-                                        "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    groups = args.rows_only.split(",") if args.rows_only else None
 
-    # --- block-wise at M = 4096 (DeepSeek-V3 shapes), weights FP8 -> requantised
-    qa_cache = {}
-    for name in ("gate_up", "down", "q_a", "q_b", "kv_a"):
-        K, N = synth.SHAPES[name]
-        codes, si = synth.fp8_weights(N, K, seed=synth.SEEDS["block"], device=dev)
-        if name == "gate_up":
-            ms = time_calls(lambda i: w8.requant_fp8_to_int8_block(codes, si), 1, 5)
-            b = N * K * 2
-            out["requant_fp8_block_gate_up"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
-                                                "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
-        wq, ws = w8.requant_fp8_to_int8_block(codes, si)
-        del codes
-        if K not in qa_cache:
-            xa = synth.activations(4096, K, seed=synth.SEEDS["block"] + 1, device=dev)
-            qa_cache[K] = w8.quant_act_group(xa)
-            del xa
-        qa, sa = qa_cache[K]
-        y = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wq, ws, out=y), 1, max(5, R // 2))
-        out[f"gemm_block_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
-        if name in ("gate_up", "down"):
-            qt = w8.quant_act_token(synth.activations(4096, K, seed=5, device=dev))
-            wqc, wsc = w8.quant_act_token(synth.weights(N, K, seed=6, device=dev))
-            ms = time_calls(lambda i: w8.gemm_w8a8_channel(qt[0], qt[1], wqc, wsc, out=y), 1, max(5, R // 2))
-            out[f"gemm_channel_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
-            for M in (128, 1024):
-                yq = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-                a0, a1 = qt[0][:M].contiguous(), qt[1][:M].contiguous()
-                ms = time_calls(lambda i: w8.gemm_w8a8_channel(a0, a1, wqc, wsc, out=yq), 1, R)
-                out[f"gemm_channel_m{M}_{name}"] = gemm_entry(ms, M, N, K, N * K)
-            del wqc, wsc, qt
-        del wq, ws, y
-    del qa_cache
-    torch.cuda.empty_cache()
+    def want(g):
+        return groups is None or g in groups
 
-    # --- decode block-wise: M in {1, 8, 32, 64}, K = 7168, N = 36864, 4 weight copies (1.06 GB)
-    K, N = GATE_UP
-    wsets = []
-    for s in range(4):
-        w = synth.weights(N, K, seed=synth.SEEDS["decode"] + s, device=dev)
-        wsets.append(w8.quant_weight_block(w))
-        del w
-    for M in (1, 8, 32, 64):
-        qa, sa = w8.quant_act_group(synth.activations(M, K, seed=M, device=dev))
-        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wsets[i][0], wsets[i][1], out=y), 4, R)
-        e = gemm_entry(ms, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
-        out[f"decode_block_m{M}"] = e
-    del wsets
-    torch.cuda.empty_cache()
+    if want("quant"):
+        # --- quantisers at M = 4096, K = 7168 (bytes: 2 in + 1 out + scales)
+        x = synth.activations(4096, 7168, seed=2, device=dev)
+        ms = time_calls(lambda i: w8.quant_act_group(x), 1, R)
+        b = 4096 * 7168 * 3 + 4096 * 56 * 4
+        out["quant_act_group_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                            "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+        ms = time_calls(lambda i: w8.quant_act_token(x), 1, R)
+        b = 4096 * 7168 * 3 + 4096 * 4
+        out["quant_act_token_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                            "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
 
-    # --- decode W8A16: Qwen3-8B-shaped linears, 20 weight copies (> 1 GB)
-    for name in ("w8a16_qkv", "w8a16_down"):
-        K, N = synth.SHAPES[name]
-        ws_ = []
-        for s in range(20):
-            w = synth.weights(N, K, seed=40 + s, device=dev, dtype=torch.float16)
-            ws_.append(w8.quant_act_group(w))
+    if want("tile"):
+        # --- block-wise at M = 4096 (DeepSeek-V3 shapes), weights FP8 -> requantised
+        qa_cache = {}
+        for name in ("gate_up", "down", "q_a", "q_b", "kv_a"):
+            K, N = synth.SHAPES[name]
+            codes, si = synth.fp8_weights(N, K, seed=synth.SEEDS["block"], device=dev)
+            if name == "gate_up":
+                ms = time_calls(lambda i: w8.requant_fp8_to_int8_block(codes, si), 1, 5)
+                b = N * K * 2
+                out["requant_fp8_block_gate_up"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                                    "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+            wq, ws = w8.requant_fp8_to_int8_block(codes, si)
+            del codes
+            if K not in qa_cache:
+                xa = synth.activations(4096, K, seed=synth.SEEDS["block"] + 1, device=dev)
+                qa_cache[K] = w8.quant_act_group(xa)
+                del xa
+            qa, sa = qa_cache[K]
+            y = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
+            ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wq, ws, out=y), 1, max(5, R // 2))
+            out[f"gemm_block_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
+            if name in ("gate_up", "down"):
+                qt = w8.quant_act_token(synth.activations(4096, K, seed=5, device=dev))
+                wqc, wsc = w8.quant_act_token(synth.weights(N, K, seed=6, device=dev))
+                ms = time_calls(lambda i: w8.gemm_w8a8_channel(qt[0], qt[1], wqc, wsc, out=y), 1, max(5, R // 2))
+                out[f"gemm_channel_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
+                for M in (128, 1024):
+                    yq = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+                    a0, a1 = qt[0][:M].contiguous(), qt[1][:M].contiguous()
+                    ms = time_calls(lambda i: w8.gemm_w8a8_channel(a0, a1, wqc, wsc, out=yq), 1, R)
+                    out[f"gemm_channel_m{M}_{name}"] = gemm_entry(ms, M, N, K, N * K)
+                del wqc, wsc, qt
+            del wq, ws, y
+        del qa_cache
+        torch.cuda.empty_cache()
+
+    if want("decode"):
+        # --- decode block-wise: M in {1, 8, 32, 64}, K = 7168, N = 36864, 4 weight copies (1.06 GB)
+        K, N = GATE_UP
+        wsets = []
+        for s in range(4):
+            w = synth.weights(N, K, seed=synth.SEEDS["decode"] + s, device=dev)
+            wsets.append(w8.quant_weight_block(w))
             del w
         for M in (1, 8, 32, 64):
-            xx = synth.activations(M, K, seed=M, device=dev, dtype=torch.float16)
-            y = torch.empty(M, N, dtype=torch.float16, device=dev)
-            ms = time_calls(lambda i: w8.gemm_w8a16_group(xx, ws_[i][0], ws_[i][1], out=y), 20, R)
-            byts = N * K + 4 * N * (K // 128) + 2 * M * K + 2 * M * N
-            out[f"decode_w8a16_{name}_m{M}"] = {"ms": round(ms, 4), "GBps": round(byts / ms / 1e6, 1),
-                                                "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
-        del ws_
-    torch.cuda.empty_cache()
-
-    # --- MoE: 256 experts, top-8 of 4096 tokens
-    E, T, TOPK = 256, 4096, 8
-    logits = synth.router_logits(T, E, seed=synth.SEEDS["moe"], device=dev)
-    rows_, _, offs = synth.route_topk(logits, TOPK)
-    P = rows_.numel()
-    for name in ("moe_gate_up", "moe_down"):
-        K, N = synth.SHAPES[name]
-        NB, KB = (N + 127) // 128, K // 128
-        Wq = torch.empty(E, N, K, dtype=torch.int8, device=dev)
-        Ws = torch.empty(E, NB, KB, dtype=torch.float32, device=dev)
-        for e0 in range(0, E, 32):
-            w = synth.weights(32 * N, K, seed=100 + e0, device=dev)
-            q, s = w8.quant_weight_block(w)
-            Wq[e0:e0 + 32] = q.view(32, N, K)
-            Ws[e0:e0 + 32] = s.view(32, NB, KB)
-            del w, q, s
-        if name == "moe_gate_up":
-            xt = synth.activations(T, K, seed=7, device=dev)
-            qa, sa = w8.quant_act_group(xt[rows_].contiguous())
-            del xt
-        else:
-            qa, sa = w8.quant_act_group(synth.activations(P, K, seed=8, device=dev))
-        y = torch.empty(P, N, dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: w8.gemm_w8a8_block_grouped(qa, sa, Wq, Ws, offs, out=y), 1, 5, warm=1)
-        ops = 2.0 * P * N * K
-        byts = E * N * K + P * K + 2 * P * N
-        out[f"gemm_block_grouped_{name}"] = {"ms": round(ms, 4), "TOPS": round(ops / ms / 1e9, 1),
-                                             "GBps": round(byts / ms / 1e6, 1),
-                                             "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
-        del Wq, Ws, qa, sa, y
+            qa, sa = w8.quant_act_group(synth.activations(M, K, seed=M, device=dev))
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wsets[i][0], wsets[i][1], out=y), 4, R)
+            e = gemm_entry(ms, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
+            out[f"decode_block_m{M}"] = e
+        del wsets
         torch.cuda.empty_cache()
+
+    if want("w8a16"):
+        # --- decode W8A16: Qwen3-8B-shaped linears, 20 weight copies (> 1 GB)
+        for name in ("w8a16_qkv", "w8a16_down"):
+            K, N = synth.SHAPES[name]
+            ws_ = []
+            for s in range(20):
+                w = synth.weights(N, K, seed=40 + s, device=dev, dtype=torch.float16)
+                ws_.append(w8.quant_act_group(w))
+                del w
+            for M in (1, 8, 32, 64):
+                xx = synth.activations(M, K, seed=M, device=dev, dtype=torch.float16)
+                y = torch.empty(M, N, dtype=torch.float16, device=dev)
+                ms = time_calls(lambda i: w8.gemm_w8a16_group(xx, ws_[i][0], ws_[i][1], out=y), 20, R)
+                byts = N * K + 4 * N * (K // 128) + 2 * M * K + 2 * M * N
+                out[f"decode_w8a16_{name}_m{M}"] = {"ms": round(ms, 4), "GBps": round(byts / ms / 1e6, 1),
+                                                    "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+            del ws_
+        torch.cuda.empty_cache()
+
+    if want("moe"):
+        # --- MoE: 256 experts, top-8 of 4096 tokens
+        E, T, TOPK = 256, 4096, 8
+        logits = synth.router_logits(T, E, seed=synth.SEEDS["moe"], device=dev)
+        rows_, _, offs = synth.route_topk(logits, TOPK)
+        P = rows_.numel()
+        for name in ("moe_gate_up", "moe_down"):
+            K, N = synth.SHAPES[name]
+            NB, KB = (N + 127) // 128, K // 128
+            Wq = torch.empty(E, N, K, dtype=torch.int8, device=dev)
+            Ws = torch.empty(E, NB, KB, dtype=torch.float32, device=dev)
+            for e0 in range(0, E, 32):
+                w = synth.weights(32 * N, K, seed=100 + e0, device=dev)
+                q, s = w8.quant_weight_block(w)
+                Wq[e0:e0 + 32] = q.view(32, N, K)
+                Ws[e0:e0 + 32] = s.view(32, NB, KB)
+                del w, q, s
+            if name == "moe_gate_up":
+                xt = synth.activations(T, K, seed=7, device=dev)
+                qa, sa = w8.quant_act_group(xt[rows_].contiguous())
+                del xt
+            else:
+                qa, sa = w8.quant_act_group(synth.activations(P, K, seed=8, device=dev))
+            y = torch.empty(P, N, dtype=torch.bfloat16, device=dev)
+            ms = time_calls(lambda i: w8.gemm_w8a8_block_grouped(qa, sa, Wq, Ws, offs, out=y), 1, 5, warm=1)
+            ops = 2.0 * P * N * K
+            byts = E * N * K + P * K + 2 * P * N
+            out[f"gemm_block_grouped_{name}"] = {"ms": round(ms, 4), "TOPS": round(ops / ms / 1e9, 1),
+                                                 "GBps": round(byts / ms / 1e6, 1),
+                                                 "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+            del Wq, Ws, qa, sa, y
+            torch.cuda.empty_cache()
     return out
 
 
