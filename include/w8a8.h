@@ -11,9 +11,10 @@
  *   q     = clamp(round_half_even(x / scale), -127, 127)   x / scale in fp32
  *
  * Conventions shared by every entry point:
- *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *     library allocates nothing and keeps no state between calls; calls are
- *     thread-safe.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  Calls
+ *     are thread-safe.  The only state the library keeps is a split-K
+ *     workspace per (device, stream) for gemm_w8a8_block / gemm_w8a8_channel
+ *     (see there); every other entry point allocates nothing.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream) and returns without synchronising.
  *     Results are visible once the stream reaches that point.
@@ -47,7 +48,7 @@ enum w8_status {
   W8_ERR_SHAPE = -2,  /* negative size, K % 128 != 0, or a size beyond the limits below */
   W8_ERR_ALIGN = -3,  /* a pointer is not aligned as required */
   W8_ERR_DTYPE = -4,  /* unsupported dtype code */
-  W8_ERR_LAUNCH = -5  /* the HIP runtime rejected a kernel launch */
+  W8_ERR_LAUNCH = -5  /* the HIP runtime rejected a kernel launch or a workspace allocation */
 };
 
 enum w8_dtype { W8_BF16 = 0, W8_FP16 = 1, W8_FP32 = 2, W8_I32 = 3 };
@@ -125,6 +126,16 @@ int requant_fp8_to_int8_channel(const uint8_t* w_fp8, const float* scale_inv,
  *   A [M][K] int8, a_scale [M][KB], W [N][K] int8, w_scale [NB][KB]
  *   Y [M][N] bf16 (y_dtype W8_BF16) or fp32 (W8_FP32).
  * The bf16 output is the round-to-nearest-even of the fp32 result.
+ * Split-K workspace (this call and gemm_w8a8_channel): when the output tile
+ * grid is too small to occupy the GPU (few tiles of 256 x 256 for M > 128,
+ * or 128 x 256 for M <= 128 block-wise), K is split into S slices whose
+ * partial tiles (S x M x N x 4 bytes) go to a device workspace that the
+ * library allocates on the first such call on a stream and grows when a
+ * later call needs more (the growth synchronises that stream); it is kept
+ * until the process ends.  The slices are summed in slice order, so results
+ * stay deterministic.  A caller that captures graphs should make one such
+ * call of the largest shape before capturing.  An allocation failure
+ * returns W8_ERR_LAUNCH with nothing enqueued.
  */
 int gemm_w8a8_block(const int8_t* A, const float* a_scale,
                     const int8_t* W, const float* w_scale,
@@ -140,6 +151,9 @@ int gemm_w8a8_block(const int8_t* A, const float* a_scale,
  *   A [M][K] int8, a_scale [M], W [N][K] int8, w_scale [N]
  *   Y [M][N] bf16, fp32, or int32 (y_dtype W8_I32: raw ACC, scales unused and
  *   may be NULL).
+ * Uses the split-K workspace described at gemm_w8a8_block for small tile
+ * grids; the int32 slice sums are exact, so the result is the same as
+ * unsplit.
  */
 int gemm_w8a8_channel(const int8_t* A, const float* a_scale,
                       const int8_t* W, const float* w_scale,

@@ -65,7 +65,7 @@ const char* w8_status_string(int status) {
     case W8_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or beyond the limits)";
     case W8_ERR_ALIGN: return "misaligned pointer (data 16-byte, scales 4-byte)";
     case W8_ERR_DTYPE: return "unsupported dtype";
-    case W8_ERR_LAUNCH: return "kernel launch failed";
+    case W8_ERR_LAUNCH: return "kernel launch or workspace allocation failed";
     default: return "unknown status";
   }
 }
