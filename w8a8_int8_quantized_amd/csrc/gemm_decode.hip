@@ -391,11 +391,12 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
       const int g = it * (PF / G) + p / G;
       const int buf = g & 1;
       const int bo = (p % G) * CHUNKS;
-      // row groups in chunks of JC: all of them at once for up to 64 rows,
-      // one at a time beyond (bounds the fragment registers)
-      constexpr int JC = MF <= 4 ? MF : 1;
+      // row groups in chunks of up to four (bounds the fragment registers
+      // beyond 64 rows), skipping chunks past the tile's rows
+      constexpr int JC = MF <= 4 ? MF : 4;
 #pragma unroll
       for (int j0 = 0; j0 < MF; j0 += JC) {
+        if (JC < MF && j0 * 16 >= M) continue;
         v4i af[JC][2];
         float saj[JC];
 #pragma unroll
@@ -919,14 +920,14 @@ hipError_t launch_gemm_block_grouped_shared(const int8_t* A, const float* sa, co
                                             int64_t N, int64_t K, hipStream_t st) {
   constexpr int NWV = 8;
   const int64_t TN = (N + 16 * NWV - 1) / (16 * NWV);
-  const int64_t TM = (P + 127) / 128 + E;  // upper bound on the experts' 128-row tiles
+  const int64_t TM = (P + 255) / 256 + E;  // upper bound on the experts' 256-row tiles
   const dim3 g((unsigned)(TM * TN));
   if (out == OUT_BF16)
-    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 8, NWV, 2, 2, OUT_BF16>), g, dim3(64 * NWV), 0, st, A, sa, W, sw,
-                       offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
+    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 16, NWV, 2, 2, OUT_BF16>), g, dim3(64 * NWV), 0, st, A, sa, W,
+                       sw, offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
   else
-    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 8, NWV, 2, 2, OUT_F32>), g, dim3(64 * NWV), 0, st, A, sa, W, sw,
-                       offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
+    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 16, NWV, 2, 2, OUT_F32>), g, dim3(64 * NWV), 0, st, A, sa, W,
+                       sw, offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
   return hipGetLastError();
 }
 
