@@ -13,8 +13,9 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  Calls
  *     are thread-safe.  The only state the library keeps is a split-K
- *     workspace per (device, stream) for gemm_w8a8_block / gemm_w8a8_channel
- *     (see there); every other entry point allocates nothing.
+ *     workspace per (device, stream) for gemm_w8a8_block, gemm_w8a8_channel
+ *     and gemm_w8a16_group (described at gemm_w8a8_block); every other entry
+ *     point allocates nothing.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream) and returns without synchronising.
  *     Results are visible once the stream reaches that point.
@@ -174,6 +175,10 @@ int gemm_w8a8_block_partials(const int8_t* A, const int8_t* W, int32_t* P,
  *   Y[m][n] = sum_g w_scale[n][g] * sum_{k in group g} x[m][k] * W[n][k]
  *   x [M][K] fp16, W [N][K] int8, w_scale [N][KB] fp32, Y [M][N] fp16.
  * Each x * W product is exact in fp32; sums are fp32.
+ * For M > 16 with few output columns per CU, K is split into S slices whose
+ * fp32 partials (S x min(M, 64) x N x 4 bytes) go to the split-K workspace
+ * described at gemm_w8a8_block and are summed in slice order: the result is
+ * deterministic, with the fp32 rounding of that order.
  */
 int gemm_w8a16_group(const uint16_t* x, const int8_t* W, const float* w_scale,
                      uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);

@@ -147,6 +147,23 @@ def test_decode_wide_block_and_channel(M, N):
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
 
 
+# N = 1000 is not a multiple of the 64-column workgroup: the last workgroup's
+# fourth wave owns no columns, and K is split over 8 workgroups (slices past
+# the first start their descriptors mid-row).  Regression case for such a wave
+# reading past its (empty) range.
+@pytest.mark.parametrize("M", [24, 32, 64])
+def test_w8a16_split_k_ragged_workgroup(M):
+    N, K = 1000, 4096
+    x = synth.activations(M, K, seed=M + 11, dtype=torch.float16)
+    w = synth.weights(N, K, seed=N + M + 1, dtype=torch.float16)
+    qw, sw = quant.quant_act_group(w.numpy())
+    y64, y32 = gemm.gemm_w8a16_group(x.numpy(), qw, sw)
+    X, W, SW = _dev(x.numpy(), qw, sw)
+    yn = _np(w8.gemm_w8a16_group(X, W, SW)).astype(np.float32)
+    e32, e64 = gemm.normwise_rel_err(yn, y32), gemm.normwise_rel_err(yn, y64)
+    assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+
+
 @pytest.mark.parametrize("M", [1, 24, 64, 80])
 def test_w8a16_wide(M):
     N, K = 12280, 640

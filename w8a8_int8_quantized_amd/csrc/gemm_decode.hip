@@ -73,12 +73,14 @@ constexpr uint32_t kOob = 0x40000000u;
 
 // Base and size are workgroup-uniform; readfirstlane states it, so the
 // descriptor stays in scalar registers (a descriptor the compiler cannot
-// prove uniform gets a loop around every load).
+// prove uniform gets a loop around every load).  A size computed as zero or
+// less (a wave past the last column in a later K slice) becomes an empty
+// range: every load through it reads zero.
 __device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
   const uint64_t a = (uint64_t)base;
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  const int n = __builtin_amdgcn_readfirstlane((int)(bytes > 0 ? bytes : 0));
   return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), 0, n, 0x00020000);
 }
 __device__ __forceinline__ v4i bl16(rsrc_t r, uint32_t off) {
@@ -629,17 +631,22 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int nw = blockIdx.x * 16 * NWV + 16 * wave;
-  const int KB = K >> 7;
+  const int KBt = K >> 7;
+  // split-K: slice blockIdx.y of gridDim.y covers K blocks kbs .. kbe - 1;
+  // every descriptor starts at the slice's first block (rows past the end
+  // still fall outside), and the slices write fp32 partials
+  const int kbs = (int)((int64_t)blockIdx.y * KBt / gridDim.y);
+  const int KB = (int)((int64_t)(blockIdx.y + 1) * KBt / gridDim.y) - kbs;
   const int NG = (KB + G - 1) / G;
   int rows = N - nw;
   rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
   const int nwc = rows > 0 ? nw : 0;
 
-  const rsrc_t rw = rsrc(W + (int64_t)nwc * K, (int64_t)rows * K);
-  const rsrc_t rs = rsrc(ws + (int64_t)nwc * KB, (int64_t)rows * KB * 4);
-  const rsrc_t rx = rsrc(x, (int64_t)M * K * 2);
+  const rsrc_t rw = rsrc(W + (int64_t)nwc * K + kbs * 128, (int64_t)rows * K - kbs * 128);
+  const rsrc_t rs = rsrc(ws + (int64_t)nwc * KBt + kbs, (int64_t)rows * KBt * 4 - kbs * 4);
+  const rsrc_t rx = rsrc(x + kbs * 128, (int64_t)M * K * 2 - kbs * 256);
   const uint32_t woff = (uint32_t)((lane & 15) * K + q * 16);
-  const uint32_t soff = (uint32_t)(4 * q * KB * 4);
+  const uint32_t soff = (uint32_t)(4 * q * KBt * 4);
   uint32_t xoff[AG];
   int xpos[AG];
 #pragma unroll
@@ -674,7 +681,7 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
     wv[P][0] = bl16(rw, woff + ko);
     wv[P][1] = bl16(rw, woff + ko + 64);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[P][r] = blf(rs, soff + r * KB * 4 + so);
+    for (int r = 0; r < 4; ++r) sv[P][r] = blf(rs, soff + r * KBt * 4 + so);
   };
 
   load_act(0);
@@ -730,6 +737,23 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
 
   const bool vec = (N & 3) == 0;
   const int n = nw + 4 * q;
+  if (gridDim.y > 1) {
+    float* yp = reinterpret_cast<float*>(Y) + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+    for (int j = 0; j < MF; ++j) {
+      const int m = 16 * j + (lane & 15);
+      if (n >= N || m >= M) continue;
+      float* y = yp + (int64_t)m * N + n;
+      if (vec && n + 3 < N) {
+        *reinterpret_cast<v4f*>(y) = facc[j];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) y[r] = facc[j][r];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < MF; ++j) {
     const int m = 16 * j + (lane & 15);
@@ -747,6 +771,25 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
       }
     }
   }
+}
+
+// Sum of S fp32 W8A16 slices in slice order, rounded to fp16 (4 outputs per
+// thread).
+__global__ __launch_bounds__(256) void k_w16_slices_sum(const float* __restrict__ part, int S, int M, int N,
+                                                        uint16_t* __restrict__ Y) {
+  const int64_t q4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nq = (N + 3) >> 2;
+  if (q4 >= (int64_t)M * nq) return;
+  const int m = (int)(q4 / nq), n = (int)(q4 - (int64_t)m * nq) * 4;
+  const int64_t idx = (int64_t)m * N + n, MN = (int64_t)M * N;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) o[r] = __fadd_rn(o[r], part[sl * MN + idx + r]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (n + r < N) Y[idx + r] = __builtin_bit_cast(uint16_t, (_Float16)o[r]);
 }
 
 // Waves per workgroup: as many as keep the whole grid resident given the
@@ -878,34 +921,33 @@ hipError_t w8a16_launch(const uint16_t* x, const int8_t* W, const float* s, uint
 
 template <int MF, int NWV, int PF>
 hipError_t w8a16_shared_launch(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M, int64_t N,
-                               int64_t K, hipStream_t st) {
-  const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)));
+                               int64_t K, int S, hipStream_t st) {
+  const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)), (unsigned)S);
   hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2, PF>), g, dim3(64 * NWV), 0, st, x, W, s, Y, M, (int)N, (int)K);
   return hipGetLastError();
 }
 
 template <int MF, int NWV>
-hipError_t w8a16_shared_depth(int pf, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M,
+hipError_t w8a16_shared_depth(int pf, int S, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M,
                               int64_t N, int64_t K, hipStream_t st) {
   if constexpr (NWV <= 4) {
-    if (pf == 8) return w8a16_shared_launch<MF, NWV, 8>(x, W, s, Y, M, N, K, st);
+    if (pf == 8) return w8a16_shared_launch<MF, NWV, 8>(x, W, s, Y, M, N, K, S, st);
   }
   if constexpr (NWV <= 8) {
-    if (pf >= 4) return w8a16_shared_launch<MF, NWV, 4>(x, W, s, Y, M, N, K, st);
+    if (pf >= 4) return w8a16_shared_launch<MF, NWV, 4>(x, W, s, Y, M, N, K, S, st);
   }
-  return w8a16_shared_launch<MF, NWV, 2>(x, W, s, Y, M, N, K, st);
+  return w8a16_shared_launch<MF, NWV, 2>(x, W, s, Y, M, N, K, S, st);
 }
 
 template <int MF>
-hipError_t w8a16_shared_width(int nwv, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M,
-                              int64_t N, int64_t K, hipStream_t st) {
-  const int pf = pick_ring_depth(N, nwv);
+hipError_t w8a16_shared_width(int nwv, int pf, int S, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y,
+                              int M, int64_t N, int64_t K, hipStream_t st) {
   switch (nwv) {
-    case 3: return w8a16_shared_depth<MF, 3>(pf, x, W, s, Y, M, N, K, st);
-    case 4: return w8a16_shared_depth<MF, 4>(pf, x, W, s, Y, M, N, K, st);
-    case 6: return w8a16_shared_depth<MF, 6>(pf, x, W, s, Y, M, N, K, st);
-    case 8: return w8a16_shared_depth<MF, 8>(pf, x, W, s, Y, M, N, K, st);
-    default: return w8a16_shared_depth<MF, 9>(pf, x, W, s, Y, M, N, K, st);
+    case 3: return w8a16_shared_depth<MF, 3>(pf, S, x, W, s, Y, M, N, K, st);
+    case 4: return w8a16_shared_depth<MF, 4>(pf, S, x, W, s, Y, M, N, K, st);
+    case 6: return w8a16_shared_depth<MF, 6>(pf, S, x, W, s, Y, M, N, K, st);
+    case 8: return w8a16_shared_depth<MF, 8>(pf, S, x, W, s, Y, M, N, K, st);
+    default: return w8a16_shared_depth<MF, 9>(pf, S, x, W, s, Y, M, N, K, st);
   }
 }
 
@@ -948,26 +990,45 @@ hipError_t launch_gemm_channel_decode(const int8_t* A, const float* sa, const in
 
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
                              int64_t K, hipStream_t st) {
-  const int nwv = pick_shared_width(N);
+  // Slices of more than 16 rows run the shared-activation kernel: width from
+  // the balance rule (4 waves where no width balances), K split over S
+  // workgroups until there are two per CU (slices of at least 4 K blocks),
+  // ring depth from the waves per CU.  The slices' fp32 partials go to the
+  // split-K workspace and are summed in order.
+  const int nwv0 = pick_shared_width(N);
+  const int nwv = nwv0 > 0 ? nwv0 : 4;
+  const int64_t wgs1 = (N + 16 * nwv - 1) / (16 * nwv);
+  const int64_t KBt = K >> 7;
+  int S = 1;
+  while (wgs1 * S < 2 * kCUs && S < 8 && KBt / (2 * S) >= 4) S *= 2;
+  const int64_t wpc = nwv * ((wgs1 * S + kCUs - 1) / kCUs);
+  const int pf = wpc <= 4 ? 8 : (wpc <= 8 ? 4 : 2);
+  float* part = nullptr;
+  if (S > 1 && M > 16) {
+    void* p = nullptr;
+    const hipError_t e = split_workspace(st, (size_t)S * (M < 64 ? M : 64) * N * 4, &p);
+    if (e != hipSuccess) return e;
+    part = static_cast<float*>(p);
+  }
   // Larger M runs as repeated 64-row slices.
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int mm = (int)(M - m0 < 64 ? M - m0 : 64);
     const uint16_t* xs = x + m0 * K;
     uint16_t* ys = Y + m0 * N;
     hipError_t e;
-    // up to 16 rows the activations are cheap to reload per wave, and the
-    // split-K kernel (more waves, no barriers) streams faster
-    if (nwv > 0 && mm > 16) {
-      if (mm <= 32)
-        e = w8a16_shared_width<2>(nwv, xs, W, s, ys, mm, N, K, st);
-      else
-        e = w8a16_shared_width<4>(nwv, xs, W, s, ys, mm, N, K, st);
-    } else if (mm <= 16) {
-      e = w8a16_launch<1, 1, 4>(xs, W, s, ys, mm, N, K, 3, st);
-    } else if (mm <= 32) {
-      e = w8a16_launch<2, 1, 2>(xs, W, s, ys, mm, N, K, 2, st);
+    if (mm > 16) {
+      uint16_t* dst = S > 1 ? reinterpret_cast<uint16_t*>(part) : ys;
+      e = mm <= 32 ? w8a16_shared_width<2>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+                   : w8a16_shared_width<4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st);
+      if (e == hipSuccess && S > 1) {
+        const dim3 rg((unsigned)((mm * ((N + 3) / 4) + 255) / 256));
+        hipLaunchKernelGGL(k_w16_slices_sum, rg, dim3(256), 0, st, part, S, mm, (int)N, ys);
+        e = hipGetLastError();
+      }
     } else {
-      e = w8a16_launch<4, 1, 1>(xs, W, s, ys, mm, N, K, 2, st);
+      // up to 16 rows the activations are cheap to reload per wave, and the
+      // split-K kernel (more waves, no barriers) streams faster
+      e = w8a16_launch<1, 1, 4>(xs, W, s, ys, mm, N, K, 3, st);
     }
     if (e != hipSuccess) return e;
   }

@@ -606,6 +606,8 @@ int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_u
   return best;
 }
 
+}  // namespace
+
 // Per-(device, stream) workspace for split-K partial tiles, grown on demand
 // and kept until the process ends.  Calls on one stream are ordered, so they
 // may share it; different streams get different buffers.
@@ -615,8 +617,10 @@ struct Workspace {
   void* p;
   size_t bytes;
 };
+namespace {
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
+}  // namespace
 
 hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) {
   int dev = 0;
@@ -648,8 +652,6 @@ hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) {
   *out = p;
   return hipSuccess;
 }
-
-}  // namespace
 
 hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {

@@ -30,6 +30,10 @@ hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
                              int64_t K, hipStream_t st);
 
+// Split-K workspace: at least `bytes` of device memory kept for `st` on the
+// current device (grown on demand; the growth synchronises `st`).
+hipError_t split_workspace(hipStream_t st, size_t bytes, void** out);
+
 // Small-M (weight-streaming) variants, used by the dispatchers above for the
 // shapes decode_path_takes accepts: every M <= 64, and channel-wise M <= 128
 // where the grid of the workgroup-shared kernel splits evenly over the CUs.
