@@ -147,6 +147,27 @@ def test_decode_wide_block_and_channel(M, N):
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
 
 
+# Five K blocks (an odd count, so the two-block activation stage of the decode
+# kernels runs one block past the row) and an infinite block scale at the
+# start of row 3: rows are independent in the block-wise definition, so every
+# other row stays finite and matches the oracle.  N = 12288 takes the
+# workgroup-shared decode kernel for M <= 64, N = 512 the split-K one, M = 200
+# the tile kernel.
+@pytest.mark.parametrize("M,N", [(8, 12288), (24, 12288), (64, 12288), (24, 512), (200, 512)])
+def test_block_rows_independent_of_next_row_scale(M, N):
+    K = 640
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M + N + 5, scheme="block")
+    sa = sa.copy()
+    sa[3, 0] = np.float32(np.inf)
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    yf = _np(w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32))
+    good = [m for m in range(M) if m != 3]
+    _, y64, y32 = gemm.gemm_block(qa[good], sa[good], qw, sw)
+    assert np.isfinite(yf[good]).all()
+    e32 = gemm.normwise_rel_err(yf[good], y32)
+    assert e32 <= 1e-5 and gemm.normwise_rel_err(yf[good], y64) <= TOL64, e32
+
+
 # N = 1000 is not a multiple of the 64-column workgroup: the last workgroup's
 # fourth wave owns no columns, and K is split over 8 workgroups (slices past
 # the first start their descriptors mid-row).  Regression case for such a wave
@@ -161,6 +182,29 @@ def test_w8a16_split_k_ragged_workgroup(M):
     X, W, SW = _dev(x.numpy(), qw, sw)
     yn = _np(w8.gemm_w8a16_group(X, W, SW)).astype(np.float32)
     e32, e64 = gemm.normwise_rel_err(yn, y32), gemm.normwise_rel_err(yn, y64)
+    assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+
+
+# Five and nine K blocks: the activation stage holds two K blocks, so the
+# last stage of a K slice has a block past the slice's end, and in the last
+# slice those bytes start the next row.  Non-finite values there must not
+# reach the row above (0 * inf); rows are independent in the definition.
+@pytest.mark.parametrize("M,N,K", [(8, 512, 640), (24, 512, 640), (32, 512, 1152), (64, 384, 1152)])
+def test_w8a16_rows_independent_of_next_row(M, N, K):
+    x = synth.activations(M, K, seed=M + K, dtype=torch.float16).numpy().copy()
+    w = synth.weights(N, K, seed=N + 7, dtype=torch.float16)
+    qw, sw = quant.quant_act_group(w.numpy())
+    bad = [3, M - 1]
+    x[3, :128] = np.float16(np.inf)
+    x[M - 1, :64] = np.float16(np.nan)
+    X, W, SW = _dev(x, qw, sw)
+    yn = _np(w8.gemm_w8a16_group(X, W, SW)).astype(np.float32)
+    good = [m for m in range(M) if m not in bad]
+    xg = np.ascontiguousarray(x[good])
+    y64, y32 = gemm.gemm_w8a16_group(xg, qw, sw)
+    assert np.isfinite(yn[good]).all()
+    e32 = gemm.normwise_rel_err(yn[good], y32)
+    e64 = gemm.normwise_rel_err(yn[good], y64)
     assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
 
 

@@ -314,14 +314,18 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
     aoff[i] = ok ? (uint32_t)(r * K + bk * 128 + col * 16) : kOob;
     apos[i] = ok ? bk * CHUNKS + r * 8 + (col ^ (r & 7)) : -1;
   }
+  // block scale i of a group: K block sbk[i] of the group; blocks past the
+  // last read zero (past the end of a row lies the next row's first scale,
+  // and an infinite one there must not reach this row through a zero partial)
   uint32_t soff[SG];
-  int spos[SG];
+  int spos[SG], sbk[SG];
 #pragma unroll
   for (int i = 0; i < SG; ++i) {
     const int e = threadIdx.x + i * NT;
     const bool ok = SMODE == 0 && e < G * ROWS;
     soff[i] = ok ? (uint32_t)((e % ROWS) * KB * 4 + (e / ROWS) * 4) : kOob;
     spos[i] = ok ? e : -1;
+    sbk[i] = e / ROWS;
   }
 
   v4f facc[FNW][MF];
@@ -338,12 +342,12 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
   float sreg[SG];
   auto load_act = [&](int g) {  // group g's activations and block scales into registers
     const uint32_t ko = g < NG ? (uint32_t)g * G * 128u : kOob;
-    const uint32_t so = g < NG ? (uint32_t)g * G * 4u : kOob;
 #pragma unroll
     for (int i = 0; i < AG; ++i) areg[i] = bl16(ra, aoff[i] + ko);
     if (SMODE == 0) {
+      const int left = KB - g * G;
 #pragma unroll
-      for (int i = 0; i < SG; ++i) sreg[i] = blf(rsa, soff[i] + so);
+      for (int i = 0; i < SG; ++i) sreg[i] = blf(rsa, soff[i] + (sbk[i] < left ? (uint32_t)g * G * 4u : kOob));
     }
   };
   auto store_act = [&](int buf) {
@@ -647,8 +651,12 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
   const rsrc_t rx = rsrc(x + kbs * 128, (int64_t)M * K * 2 - kbs * 256);
   const uint32_t woff = (uint32_t)((lane & 15) * K + q * 16);
   const uint32_t soff = (uint32_t)(4 * q * KBt * 4);
+  // activation chunk i of a group: K block xbk[i] of the group; blocks past
+  // the slice's last read zero (the bytes there belong to the next slice or,
+  // in the last slice, the next row, whose non-finite values must not reach
+  // this row through a zero weight)
   uint32_t xoff[AG];
-  int xpos[AG];
+  int xpos[AG], xbk[AG];
 #pragma unroll
   for (int i = 0; i < AG; ++i) {
     const int e = threadIdx.x + i * NT;
@@ -656,6 +664,7 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
     const bool ok = e < G * CHUNKS;
     xoff[i] = ok ? (uint32_t)(r * K * 2 + bk * 256 + col * 16) : kOob;
     xpos[i] = ok ? bk * CHUNKS + r * 16 + (col ^ (r & 15)) : -1;
+    xbk[i] = bk;
   }
 
   v4f facc[MF];
@@ -664,9 +673,12 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
 
   v4i xreg[AG];
   auto load_act = [&](int g) {
-    const uint32_t ko = g < NG ? (uint32_t)g * G * 256u : kOob;
+    const int left = KB - g * G;  // K blocks of the slice from this group on
 #pragma unroll
-    for (int i = 0; i < AG; ++i) xreg[i] = bl16(rx, xoff[i] + ko);
+    for (int i = 0; i < AG; ++i) {
+      const uint32_t ko = xbk[i] < left ? (uint32_t)g * G * 256u : kOob;
+      xreg[i] = bl16(rx, xoff[i] + ko);
+    }
   };
   auto store_act = [&](int buf) {
 #pragma unroll
