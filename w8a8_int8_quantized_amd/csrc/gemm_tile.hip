@@ -287,10 +287,12 @@ template <int BM>
 __device__ GroupTile grouped_lookup(const int32_t* __restrict__ off, int E, int P, int tmg) {
   __shared__ int scan[256];
   __shared__ int sel[3];
+  // the first ns = min(blockDim, 256) threads own contiguous runs of experts
+  // (one scan slot each); any further threads own none
   const int t = threadIdx.x;
-  const int nt = blockDim.x;
-  const int ept = (E + nt - 1) / nt;
-  const int e0 = t * ept;
+  const int ns = blockDim.x < 256 ? (int)blockDim.x : 256;
+  const int ept = (E + ns - 1) / ns;
+  const int e0 = t < ns ? t * ept : E;
   const int e1 = e0 + ept < E ? e0 + ept : E;
   int cnt = 0;
   for (int e = e0; e < e1; ++e) {
@@ -302,7 +304,7 @@ __device__ GroupTile grouped_lookup(const int32_t* __restrict__ off, int E, int 
   if (t == 0) sel[0] = -1;
   if (t < 256) scan[t] = cnt;
   __syncthreads();
-  for (int d = 1; d < nt; d <<= 1) {
+  for (int d = 1; d < ns; d <<= 1) {
     const int v = (t < 256 && t >= d) ? scan[t - d] : 0;
     __syncthreads();
     if (t < 256) scan[t] += v;
