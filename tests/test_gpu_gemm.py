@@ -68,6 +68,24 @@ def test_channel_gemm_bit_exact(M, N, K):
     assert gemm.normwise_rel_err(_np(yb.float()), y64) <= TOL64
 
 
+# Shapes whose unsplit tile grid takes the narrower channel tiles: 224 columns
+# (300 x 27990: 250 tiles in one round) and 192 columns (1000 x 12200: 256
+# tiles; 520 x 30000: 471 tiles in two rounds), each with a ragged last tile
+# in both M and N.
+@pytest.mark.parametrize("M,N,K", [(300, 27990, 256), (1000, 12200, 256), (520, 30000, 256)])
+def test_channel_gemm_narrow_tiles_bit_exact(M, N, K):
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M + N, scheme="channel")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    ACC, y64, y32 = gemm.gemm_channel(qa, sa, qw, sw)
+    acc = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)
+    assert np.array_equal(_np(acc), ACC)
+    yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
+    assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
+    yb = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+    assert gemm.normwise_rel_err(_np(yb.float()), y64) <= TOL64
+
+
 @pytest.mark.parametrize("M,N,K", [(16, 256, 256), (300, 576, 512), (129, 640, 1024)])
 def test_block_partials_bit_exact(M, N, K):
     qa, _, qw, _ = _inputs(M, N, K, seed=M + 3, scheme="block")

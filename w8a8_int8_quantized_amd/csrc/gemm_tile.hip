@@ -79,21 +79,27 @@ __device__ __forceinline__ void xcd_tile(int b, int TM, int TN, int& tm, int& tn
 }
 
 // ------------------------------------------------------------ channel-wise
-// 256 x 256 output tile per workgroup, 4 waves in a 2 (n) x 2 (m) grid, each
-// wave 128 x 128 (8 x 8 fragments of v_mfma_i32_16x16x64_i8, 256 int32
-// accumulators per lane in AGPRs).  An LDS slot holds one K block:
-// A 256 x 128 B then W 256 x 128 B.  The loop runs over 64-wide K steps; the
-// fragments of step t+1 are read from LDS while step t's 64 MFMAs run, and
-// every second step (a K block boundary) waits for the next block's DMA,
-// synchronises, and starts the DMA of the block after it.
-constexpr int kChBM = 256, kChBN = 256;
-constexpr int kChStage = (kChBM + kChBN) * 128;
+// 256 (m) x BN (n) output tile per workgroup, BN = 32 FN (FN = 8, 7 or 6);
+// 4 waves in a 2 (n) x 2 (m) grid, each wave 16 FN x 128 (FN x 8 fragments
+// of v_mfma_i32_16x16x64_i8, up to 256 int32 accumulators per lane in
+// AGPRs).  An LDS slot holds one K block: A 256 x 128 B then W BN x 128 B.
+// The loop runs over 64-wide K steps; the fragments of step t+1 are read
+// from LDS while step t's MFMAs run, and every second step (a K block
+// boundary) waits for the next block's DMA, synchronises, and starts the DMA
+// of the block after it.  Narrower tiles let the launcher fill the last
+// round of workgroups (e.g. N = 7168 at M = 4096: 448 tiles of width 256
+// leave a quarter of the second round idle, 512 tiles of width 224 do not).
+constexpr int kChBM = 256;
 
-template <int OUT>
+template <int OUT, int FN>
 __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                          void* __restrict__ Y, int M, int N, int K, int TM) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kChStage];
+  constexpr int kChBN = 32 * FN;
+  constexpr int kChStage = (kChBM + kChBN) * 128;
+  // two stages, or the bf16 epilogue's 256 rows of 512 bytes
+  constexpr int kSmem = 2 * kChStage > kChBM * 512 ? 2 * kChStage : kChBM * 512;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
@@ -112,40 +118,42 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   // still fall outside their range
   const v4i ra = make_rsrc(A + (int64_t)m0 * K + kbs * 128, (uint32_t)(mval * K - kbs * 128));
   const v4i rw = make_rsrc(W + (int64_t)n0 * K + kbs * 128, (uint32_t)(nval * K - kbs * 128));
-  const int voff = wave * 64 * K + dma_lane_off(lane, K);   // wave fills tile rows 64*wave .. +63
+  const int voff = wave * 64 * K + dma_lane_off(lane, K);        // wave fills A rows 64*wave .. +63
+  const int voffw = wave * 8 * FN * K + dma_lane_off(lane, K);   // and W rows 8*FN*wave .. +8*FN-1
   const uint32_t lds0 = lds_addr(smem);
   const int NK = kbe - kbs;
   const int K8 = 8 * K;
   const int lo0 = frag_off(lane & 15, lane >> 4);           // 16x16x64 operand: row l%16, chunk l/16
   const int lo1 = frag_off(lane & 15, 4 + (lane >> 4));
 
-  v4i acc[8][8];
+  v4i acc[FN][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
 #define CH_DMA(T)                                                                                  \
   {                                                                                               \
-    const uint32_t base = lds0 + ((T) & 1) * kChStage + wave * 8192;                              \
-    _Pragma("unroll") for (int b = 0; b < 8; ++b) dma16(ra, voff, b * K8 + (T) * 128, base + b * 1024); \
+    const uint32_t base = lds0 + ((T) & 1) * kChStage;                                            \
     _Pragma("unroll") for (int b = 0; b < 8; ++b)                                                 \
-      dma16(rw, voff, b * K8 + (T) * 128, base + kChBM * 128 + b * 1024);                         \
+      dma16(ra, voff, b * K8 + (T) * 128, base + wave * 8192 + b * 1024);                         \
+    _Pragma("unroll") for (int b = 0; b < FN; ++b)                                                \
+      dma16(rw, voffw, b * K8 + (T) * 128, base + kChBM * 128 + wave * FN * 1024 + b * 1024);     \
   }
 #define CH_RD(KS, WF, AF)                                                                          \
   {                                                                                               \
     const char* buf = smem + (((KS) >> 1) & 1) * kChStage;                                        \
     const int lo = ((KS) & 1) ? lo1 : lo0;                                                        \
     _Pragma("unroll") for (int j = 0; j < 8; ++j) AF[j] = *(const v4i*)(buf + (wm * 128 + j * 16) * 128 + lo); \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                 \
-      WF[i] = *(const v4i*)(buf + kChBM * 128 + (wn * 128 + i * 16) * 128 + lo);                  \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                                \
+      WF[i] = *(const v4i*)(buf + kChBM * 128 + (wn * 16 * FN + i * 16) * 128 + lo);              \
   }
 
   CH_DMA(0)
   waitcnt<0, 15>();
   barrier();
   if (1 < NK) CH_DMA(1)
-  v4i wc[8], ac[8];
+  v4i wc[FN], ac[8];
   CH_RD(0, wc, ac)
   for (int t = 0; t < 2 * NK; ++t) {
     if (t & 1) {
@@ -154,23 +162,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
       barrier();
       if (((t + 1) >> 1) + 1 < NK) CH_DMA(((t + 1) >> 1) + 1)
     }
-    v4i wn_[8], an_[8];
+    v4i wn_[FN], an_[8];
     CH_RD(t + 1, wn_, an_)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wc[i], ac[j], acc[i][j], 0, 0, 0);
-    // one LDS read for the next step after every 4 MFMAs
+    // one LDS read for the next step after every 4 MFMAs (the last reads of
+    // a narrower tile trail the MFMAs)
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < FN + 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      wc[i] = wn_[i];
-      ac[i] = an_[i];
-    }
+    for (int j = 0; j < 8; ++j) ac[j] = an_[j];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) wc[i] = wn_[i];
   }
 #undef CH_DMA
 #undef CH_RD
@@ -184,8 +192,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
       const int m = m0 + wm * 128 + j * 16 + (lane & 15);
       if (m >= M) continue;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+      for (int i = 0; i < FN; ++i) {
+        const int n = n0 + wn * 16 * FN + i * 16 + 4 * (lane >> 4);
         if (n < N) store4i(static_cast<int32_t*>(Y) + (int64_t)m * N + n, n, N, vec, acc[i][j]);
       }
     }
@@ -193,15 +201,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   }
   // this lane's 8 activation scales and 8 x 4 weight scales, all loads in
   // flight at once
-  float sam[8], swn[8][4];
+  float sam[8], swn[FN][4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int m = m0 + wm * 128 + j * 16 + (lane & 15);
     sam[j] = m < M ? sa[m] : 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+  for (int i = 0; i < FN; ++i) {
+    const int n = n0 + wn * 16 * FN + i * 16 + 4 * (lane >> 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) swn[i][r] = n + r < N ? sw[n + r] : 0.f;
   }
@@ -211,8 +219,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
       const int m = m0 + wm * 128 + j * 16 + (lane & 15);
       if (m >= M) continue;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+      for (int i = 0; i < FN; ++i) {
+        const int n = n0 + wn * 16 * FN + i * 16 + 4 * (lane >> 4);
         if (n >= N) continue;
         float o[4];
 #pragma unroll
@@ -224,19 +232,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   }
   // bf16: the tile goes through LDS (free now: the barrier below also means
   // every wave is past its last stage read) so that it leaves in whole rows.
-  // Tile row r holds 256 bf16 (512 bytes); its 16-byte chunk c is stored at
-  // c ^ (r & 15), so the 16 rows a write instruction touches, and the 32
-  // chunks a row read touches, fall in distinct bank groups.
+  // Tile row r holds BN bf16 in a 512-byte pitch; its 16-byte chunk c is
+  // stored at c ^ (r & 15) (< 32), so the 16 rows a write instruction
+  // touches, and the chunks a row read touches, fall in distinct bank groups.
   barrier();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = wm * 128 + j * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < FN; ++i) {
       uint32_t h[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(__fmul_rn((float)acc[i][j][q], __fmul_rn(sam[j], swn[i][q])));
-      const int chunk = wn * 16 + 2 * i + (lane >> 5);
+      const int chunk = wn * 2 * FN + 2 * i + (lane >> 5);
       *reinterpret_cast<uint2*>(smem + r * 512 + ((chunk ^ (r & 15)) << 4) + 8 * ((lane >> 4) & 1)) =
           make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
     }
@@ -244,16 +252,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   waitcnt<63, 0>();
   barrier();
   // wave w stores tile rows 64 w .. 64 w + 63, two rows per instruction;
-  // lane: row half lane >> 5, columns 8 (lane & 31) .. + 7
+  // lane: row half lane >> 5, columns 8 (lane & 31) .. + 7 (chunks past the
+  // tile's BN columns are skipped)
   const int cl = lane & 31;
   const int n = n0 + 8 * cl;
   const bool vec8 = (N & 7) == 0 && n + 7 < N;
+  const bool inside = cl < 4 * FN;
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
     const int r = wave * 64 + 2 * it + (lane >> 5);
     const int m = m0 + r;
     const v4i v = *reinterpret_cast<const v4i*>(smem + r * 512 + ((cl ^ (r & 15)) << 4));
-    if (m >= M || n >= N) continue;
+    if (m >= M || n >= N || !inside) continue;
     uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)m * N + n;
     if (vec8) {
       *reinterpret_cast<v4i*>(y) = v;
@@ -608,6 +618,47 @@ int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_u
   return best;
 }
 
+// Tile width of the unsplit channel GEMM: FN 16-column fragments per wave
+// (BN = 32 FN) in {8, 7, 6}, the smallest modelled time, where a tile costs
+// per K block ~2960 FN / 8 cycles of MFMA issue and fragment reads plus
+// ~16.5 cycles per 1 KB load instruction (32 for A, 4 FN for W), and the
+// grid runs in rounds of 256 workgroups.  Ties keep the wider tile.
+int pick_channel_width(int TM, int64_t N) {
+  int best = 8;
+  double best_t = 1e30;
+  for (int fn = 8; fn >= 6; --fn) {
+    const int64_t tiles = (int64_t)TM * ((N + 32 * fn - 1) / (32 * fn));
+    const double t = (double)((tiles + 255) / 256) * (2960.0 * fn / 8.0 + 16.5 * (32 + 4 * fn));
+    if (t < best_t * 0.98) {
+      best_t = t;
+      best = fn;
+    }
+  }
+  return best;
+}
+
+template <int FN>
+hipError_t channel_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, OutKind out,
+                          int64_t M, int64_t N, int64_t K, int TM, hipStream_t st) {
+  const int TN = (int)((N + 32 * FN - 1) / (32 * FN));
+  const dim3 grid((unsigned)(TM * TN)), block(256);
+  switch (out) {
+    case OUT_BF16:
+      hipLaunchKernelGGL((k_gemm_channel<OUT_BF16, FN>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K,
+                         TM);
+      break;
+    case OUT_F32:
+      hipLaunchKernelGGL((k_gemm_channel<OUT_F32, FN>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K,
+                         TM);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemm_channel<OUT_I32, FN>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K,
+                         TM);
+      break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Per-(device, stream) workspace for split-K partial tiles, grown on demand
@@ -658,15 +709,15 @@ hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) {
 hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (decode_path_takes(M, N, true)) return launch_gemm_channel_decode(A, sa, W, sw, Y, out, M, N, K, st);
-  const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + kChBN - 1) / kChBN);
+  const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + 255) / 256);
   // ~2.2 us per 256 x 256 tile and K block at the measured large-M rate
   const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, 2.2);
   if (S > 1) {
     void* ws = nullptr;
     hipError_t e = split_workspace(st, (size_t)S * M * N * 4, &ws);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_channel<OUT_I32>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(256), 0, st, A, sa, W,
-                       sw, ws, (int)M, (int)N, (int)K, TM);
+    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(256), 0, st, A, sa,
+                       W, sw, ws, (int)M, (int)N, (int)K, TM);
     const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
     const int32_t* wsi = static_cast<const int32_t*>(ws);
     switch (out) {
@@ -682,19 +733,12 @@ hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W
     }
     return hipGetLastError();
   }
-  dim3 grid((unsigned)(TM * TN)), block(256);
-  switch (out) {
-    case OUT_BF16:
-      hipLaunchKernelGGL((k_gemm_channel<OUT_BF16>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM);
-      break;
-    case OUT_F32:
-      hipLaunchKernelGGL((k_gemm_channel<OUT_F32>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM);
-      break;
-    default:
-      hipLaunchKernelGGL((k_gemm_channel<OUT_I32>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K, TM);
-      break;
+  const int FN = pick_channel_width(TM, N);
+  switch (FN) {
+    case 7: return channel_launch<7>(A, sa, W, sw, Y, out, M, N, K, TM, st);
+    case 6: return channel_launch<6>(A, sa, W, sw, Y, out, M, N, K, TM, st);
+    default: return channel_launch<8>(A, sa, W, sw, Y, out, M, N, K, TM, st);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
