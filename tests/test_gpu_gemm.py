@@ -121,7 +121,11 @@ def test_block_equals_channel_when_k_is_one_block():
     assert gemm.normwise_rel_err(_np(yc), yb32) <= 1e-6
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (8, 1000, 4096), (32, 512, 1024), (64, 384, 12288), (100, 256, 256)])
+# (3, 4096, 12288): the Qwen3-8B down projection at 3 rows, whose 72 KB of
+# activations are staged in LDS by the decode kernel; (12, 12288, 4096): the
+# qkv projection at 12 rows, on the shared-activation kernel split over K.
+@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (3, 4096, 12288), (8, 1000, 4096), (12, 12288, 4096),
+                                   (32, 512, 1024), (64, 384, 12288), (100, 256, 256)])
 def test_w8a16_group(M, N, K):
     x = synth.activations(M, K, seed=M, dtype=torch.float16)
     w = synth.weights(N, K, seed=N, dtype=torch.float16)
@@ -207,7 +211,7 @@ def test_w8a16_split_k_ragged_workgroup(M):
 # last stage of a K slice has a block past the slice's end, and in the last
 # slice those bytes start the next row.  Non-finite values there must not
 # reach the row above (0 * inf); rows are independent in the definition.
-@pytest.mark.parametrize("M,N,K", [(8, 512, 640), (24, 512, 640), (32, 512, 1152), (64, 384, 1152)])
+@pytest.mark.parametrize("M,N,K", [(4, 512, 640), (8, 512, 640), (24, 512, 640), (32, 512, 1152), (64, 384, 1152)])
 def test_w8a16_rows_independent_of_next_row(M, N, K):
     x = synth.activations(M, K, seed=M + K, dtype=torch.float16).numpy().copy()
     w = synth.weights(N, K, seed=N + 7, dtype=torch.float16)

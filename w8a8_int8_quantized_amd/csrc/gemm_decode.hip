@@ -503,11 +503,17 @@ __device__ __forceinline__ v8h i8x8_to_f16(uint32_t lo, uint32_t hi) {
 // v_mfma_f32_16x16x32_f16 with W as operand A.  Per 128-wide group a lane
 // loads 32 weight bytes of row n (k = 64 h + 16 q + [0, 16), h = 0, 1) and,
 // for MFMA t = 0..3, the 8 activation halves at k = 64 (t/2) + 16 q + 8 (t%2).
-template <int MF, int FNW, int SK, int PF>
+// XL (one row fragment, M <= 4): the M x K activations are staged once per
+// workgroup in dynamic LDS (M K 2 bytes, then a 256-byte zero region that
+// the fragment rows past M read), so a K block costs the weight and scale
+// loads and four LDS reads instead of four activation loads per wave.
+template <int MF, int FNW, int SK, int PF, bool XL>
 __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __restrict__ x, const int8_t* __restrict__ W,
                                                           const float* __restrict__ ws, uint16_t* __restrict__ Y, int M,
                                                           int N, int K) {
+  static_assert(!XL || MF == 1, "staged activations take one row fragment");
   __shared__ v4f red[SK][64];
+  extern __shared__ __attribute__((aligned(16))) char xs[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
@@ -526,6 +532,17 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
   }
 #pragma unroll
   for (int j = 0; j < MF; ++j) xoff[j] = (uint32_t)(((j * 16 + (lane & 15)) * K + q * 16) * 2);
+  // staged activations: row r = lane & 15 at r K 2 bytes (rows past M: the
+  // zero region, the same 256 bytes for every K block)
+  const int xr = lane & 15;
+  const uint32_t xb = XL ? (uint32_t)(xr < M ? xr * K * 2 : M * K * 2) + q * 32 : 0;
+  const uint32_t xg = xr < M ? 256u : 0u;
+  if constexpr (XL) {
+    const int nch = M * K / 8;   // 16-byte chunks of x
+    for (int i = threadIdx.x; i < nch; i += 64 * SK) reinterpret_cast<v4i*>(xs)[i] = bl16(rx, (uint32_t)i * 16);
+    if (threadIdx.x < 16) reinterpret_cast<v4i*>(xs + M * K * 2)[threadIdx.x] = (v4i){0, 0, 0, 0};
+    __syncthreads();
+  }
 
   v4f facc[FNW][MF];
 #pragma unroll
@@ -546,11 +563,17 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[P][f][r] = blf(rs, soff[f] + r * KB * 4 + so);
     }
+    if constexpr (XL) {
+      const uint32_t xo = xb + (uint32_t)(g < KB ? g : 0) * xg;
 #pragma unroll
-    for (int j = 0; j < MF; ++j)
+      for (int t = 0; t < 4; ++t) xv[P][0][t] = *reinterpret_cast<const v8h*>(xs + xo + (t >> 1) * 128 + (t & 1) * 16);
+    } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        xv[P][j][t] = __builtin_bit_cast(v8h, bl16(rx, xoff[j] + 2 * ko + (t >> 1) * 128 + (t & 1) * 16));
+      for (int j = 0; j < MF; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          xv[P][j][t] = __builtin_bit_cast(v8h, bl16(rx, xoff[j] + 2 * ko + (t >> 1) * 128 + (t & 1) * 16));
+    }
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
@@ -915,18 +938,19 @@ hipError_t decode_dispatch(const int8_t* A, const float* sa, const int8_t* W, co
   return decode_launch<MODE, 4, 2, 2, OUT>(A, sa, W, sw, Y, M, N, K, 2, st);
 }
 
-template <int MF, int FNW, int PF>
+template <int MF, int FNW, int PF, bool XL>
 hipError_t w8a16_launch(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M, int64_t N, int64_t K,
                         int waves_per_simd, hipStream_t st) {
   const int64_t wgs = (N + 16 * FNW - 1) / (16 * FNW);
   const int sk = pick_sk(wgs, K >> 7, 8, waves_per_simd);
   const dim3 g((unsigned)wgs);
   const int n = (int)N, k = (int)K;
+  const size_t lds = XL ? (size_t)M * K * 2 + 256 : 0;
   switch (sk) {
-    case 8: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 8, PF>), g, dim3(512), 0, st, x, W, s, Y, M, n, k); break;
-    case 4: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 4, PF>), g, dim3(256), 0, st, x, W, s, Y, M, n, k); break;
-    case 2: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 2, PF>), g, dim3(128), 0, st, x, W, s, Y, M, n, k); break;
-    default: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 1, PF>), g, dim3(64), 0, st, x, W, s, Y, M, n, k); break;
+    case 8: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 8, PF, XL>), g, dim3(512), lds, st, x, W, s, Y, M, n, k); break;
+    case 4: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 4, PF, XL>), g, dim3(256), lds, st, x, W, s, Y, M, n, k); break;
+    case 2: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 2, PF, XL>), g, dim3(128), lds, st, x, W, s, Y, M, n, k); break;
+    default: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 1, PF, XL>), g, dim3(64), lds, st, x, W, s, Y, M, n, k); break;
   }
   return hipGetLastError();
 }
@@ -1002,13 +1026,19 @@ hipError_t launch_gemm_channel_decode(const int8_t* A, const float* sa, const in
 
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
                              int64_t K, hipStream_t st) {
-  // Slices of more than 16 rows run the shared-activation kernel: width from
-  // the balance rule (4 waves where no width balances), K split over S
-  // workgroups until there are two per CU (slices of at least 4 K blocks),
-  // ring depth from the waves per CU.  The slices' fp32 partials go to the
-  // split-K workspace and are summed in order.
+  // Per 64-row slice: up to 4 rows the split-K decode kernel with x staged in
+  // LDS; 5..16 rows the shared-activation kernel when N balances over the CUs
+  // (its activation stage is shared by the workgroup's waves; where N does
+  // not balance, its K split and reduction cost more than the decode
+  // kernel's per-wave activation loads), else the decode kernel; more rows
+  // the shared-activation kernel.  Its width comes from the balance rule (4
+  // waves where no width balances), K is split over S workgroups until there
+  // are two per CU (slices of at least 4 K blocks), the ring depth follows the
+  // waves per CU, and the slices' fp32 partials go to the split-K workspace
+  // and are summed in order.
   const int nwv0 = pick_shared_width(N);
   const int nwv = nwv0 > 0 ? nwv0 : 4;
+  const int min_shared = nwv0 > 0 ? 5 : 17;   // fewest rows a slice takes to the shared kernel
   const int64_t wgs1 = (N + 16 * nwv - 1) / (16 * nwv);
   const int64_t KBt = K >> 7;
   int S = 1;
@@ -1016,31 +1046,31 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s,
   const int64_t wpc = nwv * ((wgs1 * S + kCUs - 1) / kCUs);
   const int pf = wpc <= 4 ? 8 : (wpc <= 8 ? 4 : 2);
   float* part = nullptr;
-  if (S > 1 && M > 16) {
+  if (S > 1 && M >= min_shared) {
     void* p = nullptr;
     const hipError_t e = split_workspace(st, (size_t)S * (M < 64 ? M : 64) * N * 4, &p);
     if (e != hipSuccess) return e;
     part = static_cast<float*>(p);
   }
-  // Larger M runs as repeated 64-row slices.
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int mm = (int)(M - m0 < 64 ? M - m0 : 64);
     const uint16_t* xs = x + m0 * K;
     uint16_t* ys = Y + m0 * N;
     hipError_t e;
-    if (mm > 16) {
+    if (mm >= min_shared) {
       uint16_t* dst = S > 1 ? reinterpret_cast<uint16_t*>(part) : ys;
-      e = mm <= 32 ? w8a16_shared_width<2>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+      e = mm <= 16 ? w8a16_shared_width<1>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+          : mm <= 32 ? w8a16_shared_width<2>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
                    : w8a16_shared_width<4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st);
       if (e == hipSuccess && S > 1) {
         const dim3 rg((unsigned)((mm * ((N + 3) / 4) + 255) / 256));
         hipLaunchKernelGGL(k_w16_slices_sum, rg, dim3(256), 0, st, part, S, mm, (int)N, ys);
         e = hipGetLastError();
       }
+    } else if (mm <= 4 && (int64_t)mm * K * 2 + 256 <= 96 * 1024) {
+      e = w8a16_launch<1, 1, 4, true>(xs, W, s, ys, mm, N, K, 3, st);
     } else {
-      // up to 16 rows the activations are cheap to reload per wave, and the
-      // split-K kernel (more waves, no barriers) streams faster
-      e = w8a16_launch<1, 1, 4>(xs, W, s, ys, mm, N, K, 3, st);
+      e = w8a16_launch<1, 1, 4, false>(xs, W, s, ys, mm, N, K, 3, st);
     }
     if (e != hipSuccess) return e;
   }
