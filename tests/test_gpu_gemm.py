@@ -230,6 +230,42 @@ def test_w8a16_rows_independent_of_next_row(M, N, K):
     assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
 
 
+# K split over workgroups with the slices reduced by the last workgroup of
+# each column tile: N not a multiple of 4 (scalar reduction), and repeated
+# calls on one stream (each call's counters must be left at zero for the next,
+# or a later call writes no output for some tiles).
+def _w8a16_case(M, N, K, seed):
+    x = synth.activations(M, K, seed=seed, dtype=torch.float16)
+    w = synth.weights(N, K, seed=seed + 1, dtype=torch.float16)
+    qw, sw = quant.quant_act_group(w.numpy())
+    return x.numpy(), qw, sw
+
+
+def test_w8a16_split_k_odd_n():
+    x, qw, sw = _w8a16_case(24, 998, 4096, seed=5)
+    y64, y32 = gemm.gemm_w8a16_group(x, qw, sw)
+    X, W, SW = _dev(x, qw, sw)
+    yn = _np(w8.gemm_w8a16_group(X, W, SW)).astype(np.float32)
+    e32, e64 = gemm.normwise_rel_err(yn, y32), gemm.normwise_rel_err(yn, y64)
+    assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+
+
+def test_w8a16_split_k_repeated_calls():
+    N, K = 12288, 4096
+    qw, sw = _w8a16_case(12, N, K, seed=9)[1:]
+    W, SW = _dev(qw, sw)
+    outs = []
+    for seed in (21, 22, 21):
+        x = synth.activations(12, K, seed=seed, dtype=torch.float16).numpy()
+        y64, y32 = gemm.gemm_w8a16_group(x, qw, sw)
+        (X,) = _dev(x)
+        yn = _np(w8.gemm_w8a16_group(X, W, SW))
+        e32 = gemm.normwise_rel_err(yn.astype(np.float32), y32)
+        assert e32 <= TOL32, (seed, e32)
+        outs.append(yn)
+    assert np.array_equal(outs[0].view(np.uint16), outs[2].view(np.uint16))
+
+
 @pytest.mark.parametrize("M", [1, 24, 64, 80])
 def test_w8a16_wide(M):
     N, K = 12280, 640
