@@ -68,6 +68,30 @@ def test_channel_gemm_bit_exact(M, N, K):
     assert gemm.normwise_rel_err(_np(yb.float()), y64) <= TOL64
 
 
+# The largest K the channel-wise entry point accepts (2^17) with codes at
+# +-127: |ACC| reaches 2^17 * 127^2 = 2,114,060,288 (row 0 of A and of W are
+# all +127), just inside int32.  M = 2 runs the decode kernel, M = 300 the
+# tile kernel split over K (int32 slice sums).
+@pytest.mark.parametrize("M,N", [(2, 256), (300, 256)])
+def test_channel_gemm_max_k_extreme_codes(M, N):
+    K = 1 << 17
+    rng = np.random.default_rng(M + N)
+    qa = (rng.integers(0, 2, (M, K), dtype=np.int8) * 2 - 1) * np.int8(127)
+    qw = (rng.integers(0, 2, (N, K), dtype=np.int8) * 2 - 1) * np.int8(127)
+    qa[0, :] = 127
+    qw[0, :] = 127
+    sa = rng.uniform(1e-3, 2e-2, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+    ACC, y64, y32 = gemm.gemm_channel(qa, sa, qw, sw)
+    assert ACC[0, 0] == K * 127 * 127
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    assert np.array_equal(_np(w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)), ACC)
+    yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
+    assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
+    yb = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+
+
 # Shapes whose unsplit tile grid takes the narrower channel tiles: 224 columns
 # (300 x 27990: 250 tiles in one round) and 192 columns (1000 x 12200: 256
 # tiles; 520 x 30000: 471 tiles in two rounds), each with a ragged last tile
