@@ -14,6 +14,10 @@ w8a8_int8_quantized_amd/libw8a8.so.  Flags:
                                       and the exact-quotient path
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                       no packed-fp32 VALU instructions
+  -mllvm -amdgpu-mfma-vgpr-form       gemm_block.hip only: MFMA results in
+                                      VGPRs, where the dequantising VALU
+                                      reads them (the channel kernel keeps its
+                                      256 accumulators per lane in AGPRs)
 """
 
 import os
@@ -28,7 +32,8 @@ LIB = os.path.join(HERE, "libw8a8.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["quant.hip", "gemm_tile.hip", "gemm_decode.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "gemm_tile.hip", "gemm_block.hip", "gemm_decode.hip", "capi.cpp"]
+EXTRA_FLAGS = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC",
     "--offload-arch=gfx950",
@@ -42,7 +47,7 @@ COMMON_FLAGS = [
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,82 +1,23 @@
-// Large-M INT8 GEMMs on gfx950 int8 MFMA.
+// Large-M channel-wise INT8 GEMM on gfx950 int8 MFMA, and the split-K
+// workspace shared with the block-wise tiles (gemm_block.hip).
 //
 // Method: "DeepSeek R1 INT8 quantisation in SGLang" (Meituan), section 2.3
-// and its Figure 3.
-//   channel-wise: Y = (A . W^T) * a_scale[m] * w_scale[n]: an all-integer K
-//                 loop, one dequantisation in the epilogue;
-//   block-wise:   the int32 partial of every 128-wide K block is dequantised
-//                 with a_scale[m][kb] * w_scale[n/128][kb] and accumulated in
-//                 fp32 inside the K loop.
+// and its Figure 3, channel-wise scheme: Y = (A . W^T) * a_scale[m] *
+// w_scale[n]: an all-integer K loop, one dequantisation in the epilogue.
 //
 // Data path (see pipeline.h): K blocks of 128 bytes per row stream
 // global -> LDS through direct-to-LDS buffer loads into a two-slot ring; the
 // load of block kb+1 is in flight while block kb is multiplied.  MFMA operand
 // A is a slice of W and operand B a slice of the activations, so each lane's
 // accumulators are consecutive output columns n of one output row m:
-// contiguous stores, one activation scale per lane and fragment, and (block
-// scheme) one weight scale per wave, because a wave's 128 columns lie inside
-// one 128-wide N block.
+// contiguous stores and one activation scale per lane and fragment.
 #include <mutex>
 #include <vector>
 
-#include "launch.h"
-#include "pipeline.h"
+#include "tile_common.h"
 
 namespace w8 {
 namespace {
-
-// Store 4 consecutive outputs Y[m][n..n+3] (n multiple of 4).
-template <int OUT>
-__device__ __forceinline__ void store4(void* Y, int64_t idx, int n, int N, bool vec, float a, float b, float c,
-                                       float d) {
-  if (OUT == OUT_F32) {
-    float* y = static_cast<float*>(Y) + idx;
-    if (vec && n + 3 < N) {
-      *reinterpret_cast<float4*>(y) = make_float4(a, b, c, d);
-    } else {
-      if (n < N) y[0] = a;
-      if (n + 1 < N) y[1] = b;
-      if (n + 2 < N) y[2] = c;
-      if (n + 3 < N) y[3] = d;
-    }
-  } else {
-    uint16_t* y = static_cast<uint16_t*>(Y) + idx;
-    const uint32_t ha = f32_to_bf16_rne(a), hb = f32_to_bf16_rne(b), hc = f32_to_bf16_rne(c),
-                   hd = f32_to_bf16_rne(d);
-    if (vec && n + 3 < N) {
-      *reinterpret_cast<uint2*>(y) = make_uint2(ha | (hb << 16), hc | (hd << 16));
-    } else {
-      if (n < N) y[0] = (uint16_t)ha;
-      if (n + 1 < N) y[1] = (uint16_t)hb;
-      if (n + 2 < N) y[2] = (uint16_t)hc;
-      if (n + 3 < N) y[3] = (uint16_t)hd;
-    }
-  }
-}
-
-__device__ __forceinline__ void store4i(int32_t* y, int n, int N, bool vec, v4i v) {
-  if (vec && n + 3 < N) {
-    *reinterpret_cast<v4i*>(y) = v;
-  } else {
-    if (n < N) y[0] = v[0];
-    if (n + 1 < N) y[1] = v[1];
-    if (n + 2 < N) y[2] = v[2];
-    if (n + 3 < N) y[3] = v[3];
-  }
-}
-
-// Workgroup -> tile.  The hardware dispatches workgroup b to XCD b % 8, and
-// each XCD has its own L2.  Tiles t = x*T/8 .. (x+1)*T/8 - 1 (M fastest) go
-// to XCD x, so an XCD owns a contiguous band of N tiles: every W panel is
-// pulled into one L2 only, and the XCD's concurrent workgroups share it.
-__device__ __forceinline__ void xcd_tile(int b, int TM, int TN, int& tm, int& tn) {
-  const int T = TM * TN;
-  const int x = b & 7, j = b >> 3;
-  const int T8 = T >> 3, rem = T & 7;
-  const int t = x * T8 + (x < rem ? x : rem) + j;
-  tm = t % TM;
-  tn = t / TM;
-}
 
 // ------------------------------------------------------------ channel-wise
 // 256 (m) x BN (n) output tile per workgroup, BN = 32 FN (FN = 8, 7 or 6);
@@ -275,281 +216,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   }
 }
 
-// -------------------------------------------------------------- block-wise
-// 256 (n) x BM (m) output tile, BM = 64 * NWM; 2 * NWM waves in a 2 (n) x NWM
-// (m) grid, each wave 128 (n) x 64 (m) as 4 x 2 fragments of
-// v_mfma_i32_32x32x32_i8.  Per K block each fragment is four chained MFMAs
-// from zero (the exact int32 partial P of that block), then
-// acc += (a_scale * w_scale) * P on the VALU; acc stays in VGPRs.  With
-// NWM = 4 two waves share each SIMD, so one wave's dequantisation overlaps
-// the other's MFMAs.
-enum { MODE_DEQUANT = 0, MODE_PARTIALS = 1, MODE_GROUPED = 2 };
-
-// Grouped GEMM: find the (expert, BM-row slice) of this workgroup's linear
-// m-tile index.  Expert e owns rows [off[e], off[e+1]) of the expert-sorted
-// activations and ceil(count / BM) m-tiles; offsets are clamped to [0, P]
-// so that no contract violation can cause an out-of-bounds access.
-struct GroupTile {
-  int e, r0, r1;   // e < 0: no tile for this workgroup
-};
-
-template <int BM>
-__device__ GroupTile grouped_lookup(const int32_t* __restrict__ off, int E, int P, int tmg) {
-  __shared__ int scan[256];
-  __shared__ int sel[3];
-  // the first ns = min(blockDim, 256) threads own contiguous runs of experts
-  // (one scan slot each); any further threads own none
-  const int t = threadIdx.x;
-  const int ns = blockDim.x < 256 ? (int)blockDim.x : 256;
-  const int ept = (E + ns - 1) / ns;
-  const int e0 = t < ns ? t * ept : E;
-  const int e1 = e0 + ept < E ? e0 + ept : E;
-  int cnt = 0;
-  for (int e = e0; e < e1; ++e) {
-    int lo = off[e], hi = off[e + 1];
-    lo = lo < 0 ? 0 : (lo > P ? P : lo);
-    hi = hi < lo ? lo : (hi > P ? P : hi);
-    cnt += (hi - lo + BM - 1) / BM;
-  }
-  if (t == 0) sel[0] = -1;
-  if (t < 256) scan[t] = cnt;
-  __syncthreads();
-  for (int d = 1; d < ns; d <<= 1) {
-    const int v = (t < 256 && t >= d) ? scan[t - d] : 0;
-    __syncthreads();
-    if (t < 256) scan[t] += v;
-    __syncthreads();
-  }
-  const int excl = (t < 256 ? scan[t] : 0) - cnt;
-  if (t < 256 && tmg >= excl && tmg < excl + cnt) {
-    int acc = excl;
-    for (int e = e0; e < e1; ++e) {
-      int lo = off[e], hi = off[e + 1];
-      lo = lo < 0 ? 0 : (lo > P ? P : lo);
-      hi = hi < lo ? lo : (hi > P ? P : hi);
-      const int c = (hi - lo + BM - 1) / BM;
-      if (tmg < acc + c) {
-        const int r0 = lo + (tmg - acc) * BM;
-        sel[0] = e;
-        sel[1] = r0;
-        sel[2] = r0 + BM < hi ? r0 + BM : hi;
-        break;
-      }
-      acc += c;
-    }
-  }
-  __syncthreads();
-  GroupTile g;
-  g.e = sel[0];
-  g.r0 = sel[1];
-  g.r1 = sel[2];
-  return g;
-}
-
-template <int MODE, int OUT, int NWM>
-__global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
-                                                             const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                             const int32_t* __restrict__ offsets, void* __restrict__ Y,
-                                                             int M, int N, int K, int TM, int TN, int E) {
-  constexpr int BM = 64 * NWM, BN = 256, NWV = 2 * NWM;
-  constexpr int STG = (BM + BN) * 128;
-  constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A (= 4)
-  constexpr int WI = BN / (8 * NWV);   // ... and for W
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STG];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
-  const int KB = K >> 7;
-  const int NB = (N + 127) >> 7;
-
-  int m0, mrows, n0;
-  const int8_t* Wx = W;
-  const float* swx = sw;
-  if (MODE == MODE_GROUPED) {
-    const int tmg = blockIdx.x / TN;
-    n0 = (blockIdx.x - tmg * TN) * BN;
-    const GroupTile g = grouped_lookup<BM>(offsets, E, M, tmg);
-    if (g.e < 0) return;
-    m0 = g.r0;
-    mrows = g.r1 - g.r0;
-    Wx = W + (int64_t)g.e * N * K;
-    swx = sw + (int64_t)g.e * NB * KB;
-  } else {
-    int tm, tn;
-    xcd_tile(blockIdx.x, TM, TN, tm, tn);
-    m0 = tm * BM;
-    n0 = tn * BN;
-    mrows = M - m0 < BM ? M - m0 : BM;
-  }
-  const int nval = N - n0 < BN ? N - n0 : BN;
-  // split-K (dequantising mode only): slice blockIdx.y of gridDim.y covers K
-  // blocks kbs .. kbe - 1 and writes its fp32 partial tile to slice
-  // blockIdx.y of Y (M x N each)
-  const int kbs = (int)((int64_t)blockIdx.y * KB / gridDim.y);
-  const int kbe = (int)((int64_t)(blockIdx.y + 1) * KB / gridDim.y);
-  if (MODE == MODE_DEQUANT) Y = static_cast<void*>(static_cast<float*>(Y) + (int64_t)blockIdx.y * M * N);
-  const v4i ra = make_rsrc(A + (int64_t)m0 * K + kbs * 128, (uint32_t)(mrows * K - kbs * 128));
-  const v4i rw = make_rsrc(Wx + (int64_t)n0 * K + kbs * 128, (uint32_t)(nval * K - kbs * 128));
-  const int voffA = wave * AI * 8 * K + dma_lane_off(lane, K);
-  const int voffW = wave * WI * 8 * K + dma_lane_off(lane, K);
-  const uint32_t lds0 = lds_addr(smem);
-  const int K8 = 8 * K;
-  int lo[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) lo[ks] = frag_off(lane & 31, 2 * ks + (lane >> 5));   // 32x32x32 operand
-
-  // this wave's 128 columns lie in one 128-wide N block
-  int nbw = (n0 + wn * 128) >> 7;
-  nbw = nbw < NB ? nbw : NB - 1;
-  const float* sw_row = swx + (int64_t)nbw * KB + kbs;
-  const float* sa_row[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = wm * 64 + j * 32 + (lane & 31);
-    sa_row[j] = sa + (int64_t)(m0 + (r < mrows ? r : mrows - 1)) * KB + kbs;
-  }
-
-  v4f facc[4][2][4];
-  if (MODE != MODE_PARTIALS) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) facc[i][j][g] = (v4f){0.f, 0.f, 0.f, 0.f};
-  }
-
-#define BK_DMA(T)                                                                                  \
-  {                                                                                               \
-    const uint32_t base = lds0 + ((T) & 1) * STG;                                                 \
-    _Pragma("unroll") for (int b = 0; b < AI; ++b)                                                \
-      dma16(ra, voffA, b * K8 + (T) * 128, base + (wave * AI + b) * 1024);                        \
-    _Pragma("unroll") for (int b = 0; b < WI; ++b)                                                \
-      dma16(rw, voffW, b * K8 + (T) * 128, base + BM * 128 + (wave * WI + b) * 1024);             \
-  }
-
-  const bool vec = (N & 3) == 0;
-  const int NKs = kbe - kbs;          // K blocks of this slice, numbered from its first
-  BK_DMA(0)
-  for (int kb = 0; kb < NKs; ++kb) {
-    waitcnt<0, 0>();                  // block kb landed (own loads); own reads of kb-1 done
-    barrier();                        // everyone's block kb landed; everyone is past kb-1
-    if (kb + 1 < NKs) BK_DMA(kb + 1)  // into the slot kb-1 used
-    const char* buf = smem + (kb & 1) * STG;
-    float s[2];
-    if (MODE != MODE_PARTIALS) {
-      const float swv = sw_row[kb];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) s[j] = __fmul_rn(sa_row[j][kb], swv);
-    }
-    v4i af[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) af[j][ks] = *(const v4i*)(buf + (wm * 64 + j * 32) * 128 + lo[ks]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v4i wf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) wf[ks] = *(const v4i*)(buf + BM * 128 + (wn * 128 + i * 32) * 128 + lo[ks]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v16i p = {};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) p = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[ks], af[j][ks], p, 0, 0, 0);
-        if (MODE == MODE_PARTIALS) {
-          const int ml = wm * 64 + j * 32 + (lane & 31);
-          if (ml < mrows) {
-            const int m = m0 + ml;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = n0 + wn * 128 + i * 32 + g * 8 + 4 * (lane >> 5);
-              if (n < N)
-                store4i(static_cast<int32_t*>(Y) + ((int64_t)kb * M + m) * N + n, n, N, vec,
-                        (v4i){p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]});
-            }
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              facc[i][j][g][r] = __builtin_fmaf(s[j], (float)p[4 * g + r], facc[i][j][g][r]);
-        }
-      }
-    }
-  }
-#undef BK_DMA
-  waitcnt<0, 15>();
-
-  if (MODE == MODE_PARTIALS) return;
-  if (OUT == OUT_BF16) {
-    // the bf16 tile goes through LDS (row r of 256 bf16, 16-byte chunk c at
-    // c ^ (r & 15)) so that it leaves in whole rows; the barrier also means
-    // every wave is past its last stage read
-    waitcnt<0, 0>();
-    barrier();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = wm * 64 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint32_t h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(facc[i][j][g][q]);
-          const int chunk = wn * 16 + i * 4 + g;
-          *reinterpret_cast<uint2*>(smem + r * 512 + ((chunk ^ (r & 15)) << 4) + 8 * (lane >> 5)) =
-              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        }
-    }
-    waitcnt<63, 0>();
-    barrier();
-    // wave w stores tile rows 32 w .. 32 w + 31, two rows per instruction
-    const int cl = lane & 31;
-    const int n = n0 + 8 * cl;
-    const bool vec8 = (N & 7) == 0 && n + 7 < N;
-#pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int r = wave * 32 + 2 * it + (lane >> 5);
-      const v4i v = *reinterpret_cast<const v4i*>(smem + r * 512 + ((cl ^ (r & 15)) << 4));
-      if (r >= mrows || n >= N) continue;
-      uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)(m0 + r) * N + n;
-      if (vec8) {
-        *reinterpret_cast<v4i*>(y) = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n + e < N) y[e] = (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1)));
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ml = wm * 64 + j * 32 + (lane & 31);
-    if (ml >= mrows) continue;
-    const int m = m0 + ml;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + i * 32 + g * 8 + 4 * (lane >> 5);
-        if (n >= N) continue;
-        store4<OUT>(Y, (int64_t)m * N + n, n, N, vec, facc[i][j][g][0], facc[i][j][g][1], facc[i][j][g][2],
-                    facc[i][j][g][3]);
-      }
-  }
-}
-
-template <int MODE, int OUT, int NWM>
-void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float* sa, const int8_t* W,
-                         const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E) {
-  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM>), grid, dim3(128 * NWM), 0, st, A, sa, W, sw, off, Y, M, N, K, TM,
-                     TN, E);
-}
-
 // ---------------------------------------------------------------- split-K
 // Sum of the S slices' partial tiles, in slice order, then the output.
 // Channel-wise: int32 slices (the sum is exact) and the channel epilogue
@@ -581,42 +247,7 @@ __global__ __launch_bounds__(256) void k_splitk_sum_i32(const int32_t* __restric
   }
 }
 
-template <int OUT>
-__global__ __launch_bounds__(256) void k_splitk_sum_f32(const float* __restrict__ ws, int S, int M, int N,
-                                                        void* __restrict__ Y) {
-  const int64_t q4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int nq = (N + 3) >> 2;
-  if (q4 >= (int64_t)M * nq) return;
-  const int m = (int)(q4 / nq), n = (int)(q4 - (int64_t)m * nq) * 4;
-  const int64_t idx = (int64_t)m * N + n;
-  const int64_t MN = (int64_t)M * N;
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int sl = 0; sl < S; ++sl)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n + r < N) o[r] = __fadd_rn(o[r], ws[sl * MN + idx + r]);
-  store4<OUT>(Y, idx, n, N, (N & 3) == 0, o[0], o[1], o[2], o[3]);
-}
 
-// Number of K slices for a tile grid that leaves CUs idle: the smallest
-// modelled time over S = 1..16, where a slice of KB / S blocks costs one
-// round of workgroups per 256, t_kb microseconds per tile and K block, and
-// splitting adds the slices' partial tiles through HBM (written and read,
-// 8 bytes per output per slice at ~5 TB/s) plus a reduction launch.
-int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us) {
-  int best = 1;
-  double best_t = 1e30;
-  for (int S = 1; S <= 16 && S <= KB; ++S) {
-    const int64_t rounds = (tiles * S + 255) / 256;
-    double t = (double)rounds * ((double)KB / S) * t_kb_us;
-    if (S > 1) t += (double)S * M * N * 8.0 / 5.0e6 + 3.0;
-    if (t < best_t * 0.97) {
-      best_t = t;
-      best = S;
-    }
-  }
-  return best;
-}
 
 // Tile width of the unsplit channel GEMM: FN 16-column fragments per wave
 // (BN = 32 FN) in {8, 7, 6}, the smallest modelled time, where a tile costs
@@ -674,6 +305,26 @@ namespace {
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
 }  // namespace
+
+// Number of K slices for a tile grid that leaves CUs idle: the smallest
+// modelled time over S = 1..16, where a slice of KB / S blocks costs one
+// round of workgroups per 256, t_kb microseconds per tile and K block, and
+// splitting adds the slices' partial tiles through HBM (written and read,
+// 8 bytes per output per slice at ~5 TB/s) plus a reduction launch.
+int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us) {
+  int best = 1;
+  double best_t = 1e30;
+  for (int S = 1; S <= 16 && S <= KB; ++S) {
+    const int64_t rounds = (tiles * S + 255) / 256;
+    double t = (double)rounds * ((double)KB / S) * t_kb_us;
+    if (S > 1) t += (double)S * M * N * 8.0 / 5.0e6 + 3.0;
+    if (t < best_t * 0.97) {
+      best_t = t;
+      best = S;
+    }
+  }
+  return best;
+}
 
 hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) {
   int dev = 0;
@@ -739,71 +390,6 @@ hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W
     case 6: return channel_launch<6>(A, sa, W, sw, Y, out, M, N, K, TM, st);
     default: return channel_launch<8>(A, sa, W, sw, Y, out, M, N, K, TM, st);
   }
-}
-
-hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
-                             OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (decode_path_takes(M, N, false)) return launch_gemm_block_decode(A, sa, W, sw, Y, out, M, N, K, st);
-  const int TN = (int)((N + 255) / 256);
-  const int BM = M <= 128 ? 128 : 256;
-  const int TM = (int)((M + BM - 1) / BM);
-  // ~3.3 us per 256 x 256 tile and K block at the measured large-M rate
-  const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, BM == 256 ? 3.3 : 1.9);
-  void* dst = Y;
-  if (S > 1) {
-    hipError_t e = split_workspace(st, (size_t)S * M * N * 4, &dst);
-    if (e != hipSuccess) return e;
-  }
-  const dim3 grid((unsigned)(TM * TN), (unsigned)S);
-  const bool f32 = S > 1 || out == OUT_F32;
-  if (BM == 128) {
-    if (f32)
-      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
-    else
-      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
-  } else {
-    if (f32)
-      launch_block_kernel<MODE_DEQUANT, OUT_F32, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
-    else
-      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM, TN, 0);
-  }
-  if (S > 1) {
-    const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
-    const float* wsf = static_cast<const float*>(dst);
-    if (out == OUT_BF16)
-      hipLaunchKernelGGL((k_splitk_sum_f32<OUT_BF16>), rg, dim3(256), 0, st, wsf, S, (int)M, (int)N, Y);
-    else
-      hipLaunchKernelGGL((k_splitk_sum_f32<OUT_F32>), rg, dim3(256), 0, st, wsf, S, (int)M, (int)N, Y);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
-                                      hipStream_t st) {
-  const int TM = (int)((M + 255) / 256), TN = (int)((N + 255) / 256);
-  launch_block_kernel<MODE_PARTIALS, OUT_I32, 4>(dim3((unsigned)(TM * TN)), st, A, nullptr, W, nullptr, nullptr, P,
-                                                 (int)M, (int)N, (int)K, TM, TN, 0);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
-                                     const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P, int64_t N,
-                                     int64_t K, hipStream_t st) {
-  // few rows per expert: the expert weights are streamed once per 128-row
-  // tile, and the weight stream sets the pace
-  if (E > 0 && P <= 256 * E)
-    return launch_gemm_block_grouped_shared(A, sa, W, sw, offsets, Y, out, E, P, N, K, st);
-  // upper bound on the number of 128-row m-tiles over all experts
-  const int64_t TMmax = (P + 127) / 128 + E;
-  const int TN = (int)((N + 255) / 256);
-  dim3 grid((unsigned)(TMmax * TN));
-  if (out == OUT_BF16)
-    launch_block_kernel<MODE_GROUPED, OUT_BF16, 2>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
-                                                   (int)TMmax, TN, (int)E);
-  else
-    launch_block_kernel<MODE_GROUPED, OUT_F32, 2>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
-                                                  (int)TMmax, TN, (int)E);
-  return hipGetLastError();
 }
 
 }  // namespace w8

@@ -33,6 +33,9 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s,
 // Split-K workspace: at least `bytes` of device memory kept for `st` on the
 // current device (grown on demand; the growth synchronises `st`).
 hipError_t split_workspace(hipStream_t st, size_t bytes, void** out);
+// Number of K slices (1..16) for a grid of `tiles` workgroups over KB K
+// blocks, from a model with t_kb_us microseconds per tile and K block.
+int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us);
 
 // Small-M (weight-streaming) variants, used by the dispatchers above for the
 // shapes decode_path_takes accepts: every M <= 64, and channel-wise M <= 128
