@@ -326,13 +326,11 @@ def test_tile_gemms_full_grid_unsplit():
 
 
 # Grouped (MoE) cases: (experts, tokens, top-k, K, N, experts given no
-# tokens, expert made hot).  Few rows per expert (at most 256 on average)
-# run the weight-streaming kernel over 128-row expert tiles (the hot expert
-# spans several tiles; 300 experts is more than the tile lookup's 64 lanes x
-# 4); more rows per expert run the LDS-tiled kernel, with 128-row tiles below
-# 512 rows per expert on average (8 experts, 3072 rows, one empty, one hot)
-# and 256-row tiles from there (4 experts, 2048 rows).  N = 400 and N = 300
-# leave a ragged last weight block.
+# tokens, expert made hot).  Expert row ranges are cut into 128-row tiles
+# below 96 rows per expert on average and 256-row tiles from there; the hot
+# expert spans several tiles, 300 experts is more than the tile lookup's 64
+# lanes x 4, and 256-row tiles of experts with fewer rows leave whole waves
+# idle.  N = 400 and N = 300 leave a ragged last weight block.
 GROUPED_CASES = [
     (12, 200, 2, 512, 384, (5, 7), None),
     (40, 1024, 4, 640, 400, (), 3),

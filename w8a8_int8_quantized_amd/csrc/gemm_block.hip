@@ -136,11 +136,15 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     }
   };
 
+  // 8-row groups of A past the tile's rows are not loaded (their LDS rows
+  // feed only outputs that are never stored), and a wave whose 64 rows all
+  // lie past them skips its MFMAs (MoE expert tiles are often part-empty)
+  const bool wact = wm * 64 < mrows;
 #define BK_DMA(T)                                                                                  \
   {                                                                                               \
     const uint32_t base = lds0 + ((T) & 1) * STG;                                                 \
     _Pragma("unroll") for (int b = 0; b < AI; ++b)                                                \
-      dma16(ra, voffA, b * K8 + (T) * 128, base + (wave * AI + b) * 1024);                        \
+      if ((wave * AI + b) * 8 < mrows) dma16(ra, voffA, b * K8 + (T) * 128, base + (wave * AI + b) * 1024); \
     _Pragma("unroll") for (int b = 0; b < WI; ++b)                                                \
       dma16(rw, voffW, b * K8 + (T) * 128, base + BM * 128 + (wave * WI + b) * 1024);             \
   }
@@ -168,6 +172,7 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
       la1 = sa_t[sao[1] + kn];
       lw = sw_row[kn];
     }
+    if (!wact) continue;
     const char* buf = smem + (kb & 1) * STG;
     v4i af[2][4], wc[4], wnx[4];
 #pragma unroll
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     sp = sc1;
   }
 #undef BK_DMA
-  if (NK > 0) drain(pp, std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}, sp, NK - 1);
+  if (NK > 0 && wact) drain(pp, std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}, sp, NK - 1);
   waitcnt<0, 0>();
   if (!DQ) return;
 
@@ -362,14 +367,13 @@ hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t*
 hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
                                      const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P, int64_t N,
                                      int64_t K, hipStream_t st) {
-  // few rows per expert: the expert weights are streamed once per 128-row
-  // tile, and the weight stream sets the pace
-  if (E > 0 && P <= 256 * E)
-    return launch_gemm_block_grouped_shared(A, sa, W, sw, offsets, Y, out, E, P, N, K, st);
+  // Every expert tile streams its expert's weight panel once, so even at a
+  // few rows per expert this runs at the weight stream's pace; waves whose
+  // rows are all past the expert's rows skip their MFMAs.  256-row tiles from
+  // 96 rows per expert on average (fewer second tiles re-reading a panel),
+  // 128-row tiles below.
   const int TN = (int)((N + 255) / 256);
-  // 256-row tiles once experts average 512 rows or more (their ragged last
-  // tiles then waste less than the 128-row tiles' lower MFMA rate)
-  const bool big = P >= 512 * E;
+  const bool big = P >= 96 * E;
   const int BM = big ? 256 : 128;
   // upper bound on the number of m-tiles over all experts
   const int64_t TMmax = (P + BM - 1) / BM + E;

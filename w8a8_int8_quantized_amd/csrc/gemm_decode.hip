@@ -19,7 +19,6 @@
 #include "common.h"
 #include "launch.h"
 #include "pipeline.h"
-#include "grouped.h"
 
 namespace w8 {
 namespace {
@@ -29,9 +28,6 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 // SIMDs per GPU the dispatchers size grids against (256 CUs x 4).
 constexpr int kSimds = 256 * 4;
 constexpr int kCUs = 256;
-// Mode of k_decode_shared beside 0 (block-wise) and 1 (channel-wise):
-// block-wise over experts' row tiles.
-constexpr int MODE_GROUPED_SH = 2;
 
 // Store 4 consecutive outputs of row m (n multiple of 4).
 template <int OUT>
@@ -255,15 +251,13 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restric
 template <int MODE, int MF, int NWV, int G, int PF, int OUT>
 __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                         const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                        const int32_t* __restrict__ offsets, void* __restrict__ Y,
-                                                        int M, int N, int K, int E, int TN) {
+                                                        void* __restrict__ Y, int M, int N, int K) {
   constexpr int FNW = 1;
   constexpr int ROWS = 16 * MF;                                  // activation rows per block
   constexpr int CHUNKS = ROWS * 8;                               // 16-byte chunks per block
   constexpr int NT = 64 * NWV;                                   // threads
   constexpr int AG = (G * CHUNKS + NT - 1) / NT;                 // chunks per thread per group
   constexpr int SG = (G * ROWS + NT - 1) / NT;                   // block scales per thread per group
-  constexpr int SMODE = MODE == MODE_GROUPED_SH ? 0 : MODE;      // arithmetic: 0 block-wise, 1 channel-wise
   __shared__ v4i as[2][G * CHUNKS];
   __shared__ float ss[2][G * ROWS];
   const int lane = threadIdx.x & 63;
@@ -271,22 +265,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
   const int q = lane >> 4;
   const int KB = K >> 7;
   const int NG = (KB + G - 1) / G;
-  int cg = blockIdx.x;
-  if (MODE == MODE_GROUPED_SH) {
-    // workgroup = (128-row tile of one expert, column group); rows of the
-    // tile are rows r0 .. r1 - 1 of the permuted activations and outputs
-    const int t = blockIdx.x / TN;
-    cg = blockIdx.x - t * TN;
-    const ExpertTile et = group_tile<ROWS>(offsets, E, M, t);
-    if (et.e < 0) return;
-    const int NB = (N + 127) >> 7;
-    A += (int64_t)et.r0 * K;
-    sa += (int64_t)et.r0 * KB;
-    Y = static_cast<void*>(static_cast<char*>(Y) + (int64_t)et.r0 * N * (OUT == OUT_BF16 ? 2 : 4));
-    W += (int64_t)et.e * N * K;
-    sw += (int64_t)et.e * NB * KB;
-    M = et.r1 - et.r0;
-  }
+  const int cg = blockIdx.x;
   const int n0 = cg * 16 * FNW * NWV;
   const int nw = n0 + 16 * FNW * wave;
   int rows = N - nw;
@@ -322,7 +301,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
 #pragma unroll
   for (int i = 0; i < SG; ++i) {
     const int e = threadIdx.x + i * NT;
-    const bool ok = SMODE == 0 && e < G * ROWS;
+    const bool ok = MODE == 0 && e < G * ROWS;
     soff[i] = ok ? (uint32_t)((e % ROWS) * KB * 4 + (e / ROWS) * 4) : kOob;
     spos[i] = ok ? e : -1;
     sbk[i] = e / ROWS;
@@ -344,7 +323,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
     const uint32_t ko = g < NG ? (uint32_t)g * G * 128u : kOob;
 #pragma unroll
     for (int i = 0; i < AG; ++i) areg[i] = bl16(ra, aoff[i] + ko);
-    if (SMODE == 0) {
+    if (MODE == 0) {
       const int left = KB - g * G;
 #pragma unroll
       for (int i = 0; i < SG; ++i) sreg[i] = blf(rsa, soff[i] + (sbk[i] < left ? (uint32_t)g * G * 4u : kOob));
@@ -354,7 +333,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
 #pragma unroll
     for (int i = 0; i < AG; ++i)
       if (apos[i] >= 0) as[buf][apos[i]] = areg[i];
-    if (SMODE == 0) {
+    if (MODE == 0) {
 #pragma unroll
       for (int i = 0; i < SG; ++i)
         if (spos[i] >= 0) ss[buf][spos[i]] = sreg[i];
@@ -369,7 +348,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
       wv[P][f][0] = bl16(rw, woff[f] + ko);
       wv[P][f][1] = bl16(rw, woff[f] + ko + 64);
     }
-    if (SMODE == 0) swv[P] = blf(rsw, kb < KB ? (uint32_t)kb * 4u : kOob);
+    if (MODE == 0) swv[P] = blf(rsw, kb < KB ? (uint32_t)kb * 4u : kOob);
   };
 
   // prologue, issued in the order the loop issues: group 0 staged, then the
@@ -410,14 +389,14 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
           const int r = 16 * (j0 + jj) + (lane & 15);
           af[jj][0] = as[buf][bo + r * 8 + (q ^ (r & 7))];
           af[jj][1] = as[buf][bo + r * 8 + ((4 + q) ^ (r & 7))];
-          if (SMODE == 0) saj[jj] = ss[buf][(p % G) * ROWS + r];
+          if (MODE == 0) saj[jj] = ss[buf][(p % G) * ROWS + r];
         }
 #pragma unroll
         for (int f = 0; f < FNW; ++f)
 #pragma unroll
           for (int jj = 0; jj < JC; ++jj) {
             const int j = j0 + jj;
-            if (SMODE == 0) {
+            if (MODE == 0) {
               v4i pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], af[jj][0], (v4i){0, 0, 0, 0}, 0, 0, 0);
               pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], af[jj][1], pp, 0, 0, 0);
               const float s = __fmul_rn(saj[jj], swv[p]);
@@ -454,7 +433,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
       const int m = 16 * j + (lane & 15);
       if (n < N && m < M) {
         float o[4];
-        if (SMODE == 0) {
+        if (MODE == 0) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[r] = facc[f][j][r];
           store_out4<OUT>(Y, (int64_t)m * N + n, n, N, vec, o);
@@ -869,8 +848,8 @@ template <int MODE, int MF, int NWV, int PF, int OUT>
 hipError_t shared_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
                          int64_t N, int64_t K, hipStream_t st) {
   const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)));
-  hipLaunchKernelGGL((k_decode_shared<MODE, MF, NWV, 2, PF, OUT>), g, dim3(64 * NWV), 0, st, A, sa, W, sw, nullptr, Y,
-                     (int)M, (int)N, (int)K, 0, 0);
+  hipLaunchKernelGGL((k_decode_shared<MODE, MF, NWV, 2, PF, OUT>), g, dim3(64 * NWV), 0, st, A, sa, W, sw, Y,
+                     (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -991,22 +970,6 @@ hipError_t w8a16_shared_width(int nwv, int pf, int S, const uint16_t* x, const i
 
 bool decode_path_takes(int64_t M, int64_t N, bool channel) {
   return M <= 64 || (channel && M <= 128 && pick_shared_width(N) > 0);
-}
-
-hipError_t launch_gemm_block_grouped_shared(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
-                                            const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P,
-                                            int64_t N, int64_t K, hipStream_t st) {
-  constexpr int NWV = 8;
-  const int64_t TN = (N + 16 * NWV - 1) / (16 * NWV);
-  const int64_t TM = (P + 255) / 256 + E;  // upper bound on the experts' 256-row tiles
-  const dim3 g((unsigned)(TM * TN));
-  if (out == OUT_BF16)
-    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 16, NWV, 2, 2, OUT_BF16>), g, dim3(64 * NWV), 0, st, A, sa, W,
-                       sw, offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
-  else
-    hipLaunchKernelGGL((k_decode_shared<MODE_GROUPED_SH, 16, NWV, 2, 2, OUT_F32>), g, dim3(64 * NWV), 0, st, A, sa, W,
-                       sw, offsets, Y, (int)P, (int)N, (int)K, (int)E, (int)TN);
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm_block_decode(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,

@@ -45,10 +45,5 @@ hipError_t launch_gemm_block_decode(const int8_t* A, const float* sa, const int8
                                     OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm_channel_decode(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                       OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
-// Grouped block-wise GEMM over experts' 128-row tiles with weight streaming,
-// for few rows per expert.
-hipError_t launch_gemm_block_grouped_shared(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
-                                            const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P,
-                                            int64_t N, int64_t K, hipStream_t st);
 
 }  // namespace w8
