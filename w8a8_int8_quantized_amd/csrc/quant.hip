@@ -34,36 +34,27 @@ __device__ __forceinline__ void unpack8(const uint4& c, float* v) {
   }
 }
 
-// OCP FP8-E4M3FN byte -> fp32, times 2^-120.  The 7 magnitude bits moved to
-// bit 20 form an fp32 whose exponent field is e and mantissa m/8:
-//   e >= 1: 2^(e-127) (1 + m/8)  = value * 2^-120
-//   e == 0: m/8 * 2^-126 (an fp32 subnormal) = value * 2^-120
-// so one exact multiply by 2^120 recovers the value.
-__device__ __forceinline__ float fp8_scaled_down(uint32_t byte_in_low_bits) {
-  uint32_t b = byte_in_low_bits & 0xffu;
-  uint32_t bits = ((b & 0x7fu) << 20) | ((b & 0x80u) << 24);
-  return __uint_as_float(bits);
+// OCP FP8-E4M3FN byte J of w -> fp32 (exact: gfx950's v_cvt_f32_fp8 decodes
+// the OCP encoding, bias 7, subnormals included; the GPU tests cover every
+// finite code), times scale_inv in fp32, rounded to bf16 (nearest even);
+// returned as the fp32 value of that bf16 (its bit pattern is the top half).
+template <int J>
+__device__ __forceinline__ float fp8_to_bf16_value(uint32_t w, float scale_inv) {
+  const float p = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)w, J), scale_inv);
+  const uint32_t u = __float_as_uint(p);
+  return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
 }
 
-constexpr float kTwo120 = 1.329227995784916e36f;   // 2^120, exact
-
-// fp32(decode(code) * scale_inv) rounded to bf16 (nearest even), returned
-// as the fp32 value of that bf16 and its 16-bit pattern.
-__device__ __forceinline__ float fp8_to_bf16_value(uint32_t byte, float scale_inv, uint32_t* bits16) {
-  float v = __fmul_rn(fp8_scaled_down(byte), kTwo120);        // exact decode
-  float p = __fmul_rn(v, scale_inv);
-  uint32_t h = f32_to_bf16_rne(p);
-  *bits16 = h;
-  return __uint_as_float(h << 16);
-}
-
-// 16 values (and their bf16 patterns) from a 16-byte chunk of FP8 codes.
-__device__ __forceinline__ void unpack16_fp8(const uint4& c, float scale_inv, float* v, uint32_t* bf) {
+// 16 values from a 16-byte chunk of FP8 codes.
+__device__ __forceinline__ void unpack16_fp8(const uint4& c, float scale_inv, float* v) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[4 * i + j] = fp8_to_bf16_value(w[i] >> (8 * j), scale_inv, &bf[4 * i + j]);
+  for (int i = 0; i < 4; ++i) {
+    v[4 * i + 0] = fp8_to_bf16_value<0>(w[i], scale_inv);
+    v[4 * i + 1] = fp8_to_bf16_value<1>(w[i], scale_inv);
+    v[4 * i + 2] = fp8_to_bf16_value<2>(w[i], scale_inv);
+    v[4 * i + 3] = fp8_to_bf16_value<3>(w[i], scale_inv);
+  }
 }
 
 __device__ __forceinline__ float amax_n(const float* v, int n) {
@@ -131,8 +122,7 @@ struct RowFmt {
 template <int FMT>
 __device__ __forceinline__ void chunk_values(const uint4& c, float si, float* v) {
   if constexpr (FMT == FMT_FP8) {
-    uint32_t bf[16];
-    unpack16_fp8(c, si, v, bf);
+    unpack16_fp8(c, si, v);
   } else {
     unpack8<FMT == FMT_FP16>(c, v);
   }
@@ -246,62 +236,122 @@ __global__ __launch_bounds__(256) void k_quant_tile_bf16(const uint4* __restrict
   if (threadIdx.x == 0) scale[(int64_t)nb * KB + kb] = sc.s;
 }
 
-// FP8 input: the tile is 128 rows x 128 bytes = 1024 chunks, 4 per thread:
-// thread t takes column chunk t & 7 of rows (t >> 3) + 32 i.
+// FP8 input: one 256-thread workgroup per strip of 128 rows x 4 K blocks
+// (4 tiles, 64 KB of codes, all loaded up front).  Thread t takes the 16-byte
+// column chunk t & 31 of rows (t >> 5) + 8 i, i < 16: every row is read as
+// 512 contiguous bytes, and all 16 chunks of a thread lie in tile
+// (t & 31) >> 3.  Inside a tile every value is bf16(decode(code) *
+// scale_inv) with one scale_inv, so its INT8 code is a function of the FP8
+// byte alone: the tile amax comes from the codes (a finite code's magnitude
+// increases with its low 7 bits, and the fp32 product and the bf16 rounding
+// are monotone, so the largest |value| is that of the largest low-7-bit
+// code), then each thread quantises one byte value per tile with the exact
+// quotient rule into a 256-entry table, and the elements are looked up.
+// (Quantising element by element, FP8 values often sit exactly on a
+// half-integer of the grid, e.g. half the tile's largest value lands on 63.5,
+// and the exact-quotient fallback then runs for most waves.)
+constexpr int kStripTiles = 4;
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Max over the 8 lanes of each half of a 16-lane DPP row, unsigned integers.
+__device__ __forceinline__ uint32_t max8u(uint32_t v) {
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  return v;
+}
+
 template <bool WRITE_BF16>
 __global__ __launch_bounds__(256) void k_requant_tile_fp8(const uint4* __restrict__ w, const float* __restrict__ scale_inv,
                                                           int8_t* __restrict__ q, float* __restrict__ scale,
                                                           uint16_t* __restrict__ wbf, int N, int K) {
-  __shared__ float red[4];
+  __shared__ uint32_t red[4][kStripTiles];
+  __shared__ uint8_t lut[kStripTiles][256];
+  __shared__ uint16_t lutb[WRITE_BF16 ? kStripTiles : 1][256];
   const int KB = K >> 7;
-  const int kb = (int)(blockIdx.x % (unsigned)KB), nb = (int)(blockIdx.x / (unsigned)KB);
-  const int cc = threadIdx.x & 7;
+  const int NS = (KB + kStripTiles - 1) / kStripTiles;
+  const int sb = (int)(blockIdx.x % (unsigned)NS), nb = (int)(blockIdx.x / (unsigned)NS);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cc = threadIdx.x & 31;
+  const int tile = cc >> 3;
+  const int kb = sb * kStripTiles + tile;          // this thread's K block
+  const bool kok = kb < KB;
+  const int kbc = kok ? kb : KB - 1;               // clamped: threads past the last block load a valid one
   const int nchr = K >> 4;
-  const float si = scale_inv[(int64_t)nb * KB + kb];
-  uint4 raw[4];
+  uint4 raw[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = nb * 128 + (threadIdx.x >> 3) + 32 * i;
-    int rl = r < N ? r : N - 1;
-    raw[i] = w[(int64_t)rl * nchr + kb * 8 + cc];
+  for (int i = 0; i < 16; ++i) {
+    const int r = nb * 128 + (threadIdx.x >> 5) + 8 * i;
+    const int rl = r < N ? r : N - 1;
+    raw[i] = w[(int64_t)rl * nchr + kbc * 8 + (cc & 7)];
   }
-  float v[4][16];
-  uint32_t bf[4][16];
-  float a = 0.f;
+  // largest low-7-bit code of this thread's rows (bytes as u16 pairs)
+  v2u16 mlo = {0, 0}, mhi = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = nb * 128 + (threadIdx.x >> 3) + 32 * i;
-    unpack16_fp8(raw[i], si, v[i], bf[i]);
-    if (r < N) a = fmaxf(a, amax_n(v[i], 16));
-  }
-  a = block_max256(a, red);
-  QScale sc = make_scale(a);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = nb * 128 + (threadIdx.x >> 3) + 32 * i;
-    float t[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) t[e] = quant_one(v[i][e], sc);
+  for (int i = 0; i < 16; ++i) {
+    const int r = nb * 128 + (threadIdx.x >> 5) + 8 * i;
     if (r < N) {
-      uint4 o;
-      o.x = pack4(t[0], t[1], t[2], t[3]);
-      o.y = pack4(t[4], t[5], t[6], t[7]);
-      o.z = pack4(t[8], t[9], t[10], t[11]);
-      o.w = pack4(t[12], t[13], t[14], t[15]);
-      reinterpret_cast<uint4*>(q + (int64_t)r * K + kb * 128)[cc] = o;
-      if (WRITE_BF16) {
-        uint4 b0, b1;
-        b0.x = bf[i][0] | (bf[i][1] << 16);   b0.y = bf[i][2] | (bf[i][3] << 16);
-        b0.z = bf[i][4] | (bf[i][5] << 16);   b0.w = bf[i][6] | (bf[i][7] << 16);
-        b1.x = bf[i][8] | (bf[i][9] << 16);   b1.y = bf[i][10] | (bf[i][11] << 16);
-        b1.z = bf[i][12] | (bf[i][13] << 16); b1.w = bf[i][14] | (bf[i][15] << 16);
-        uint4* dst = reinterpret_cast<uint4*>(wbf + (int64_t)r * K + kb * 128) + 2 * cc;
-        dst[0] = b0;
-        dst[1] = b1;
+      const uint32_t wv[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t m = wv[k] & 0x7f7f7f7fu;
+        mlo = __builtin_elementwise_max(mlo, __builtin_bit_cast(v2u16, m & 0x00ff00ffu));
+        mhi = __builtin_elementwise_max(mhi, __builtin_bit_cast(v2u16, (m >> 8) & 0x00ff00ffu));
       }
     }
   }
-  if (threadIdx.x == 0) scale[(int64_t)nb * KB + kb] = sc.s;
+  const v2u16 mm = __builtin_elementwise_max(mlo, mhi);
+  uint32_t code = mm[0] > mm[1] ? mm[0] : mm[1];
+  // tile maximum: octet (8 lanes), then octets o and o + 4 of the wave, then waves
+  code = max8u(code);
+  {
+    // lane t < 4 collects tile t from lanes 8 t and 32 + 8 t
+    const uint32_t lo = __shfl(code, 8 * (lane & 3), 64), hi = __shfl(code, 32 + 8 * (lane & 3), 64);
+    if (lane < kStripTiles) red[wave][lane] = lo > hi ? lo : hi;
+  }
+  __syncthreads();
+  // thread c quantises byte value c for each tile of the strip
+#pragma unroll
+  for (int tt = 0; tt < kStripTiles; ++tt) {
+    const uint32_t mc = umax(umax(red[0][tt], red[1][tt]), umax(red[2][tt], red[3][tt]));
+    const int kt = sb * kStripTiles + tt < KB ? sb * kStripTiles + tt : KB - 1;
+    const float sit = scale_inv[(int64_t)nb * KB + kt];
+    const QScale sc = make_scale(__builtin_fabsf(fp8_to_bf16_value<0>(mc, __builtin_fabsf(sit))));
+    const float x = fp8_to_bf16_value<0>(threadIdx.x, sit);
+    lut[tt][threadIdx.x] = (uint8_t)(int)quant_one(x, sc);
+    if (WRITE_BF16) lutb[tt][threadIdx.x] = (uint16_t)(__float_as_uint(x) >> 16);
+    if (threadIdx.x == 0 && sb * kStripTiles + tt < KB) scale[(int64_t)nb * KB + sb * kStripTiles + tt] = sc.s;
+  }
+  __syncthreads();
+  if (!kok) return;
+  const uint8_t* lt = lut[tile];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = nb * 128 + (threadIdx.x >> 5) + 8 * i;
+    if (r < N) {
+      const uint32_t wv[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = (uint32_t)lt[wv[k] & 0xff] | ((uint32_t)lt[(wv[k] >> 8) & 0xff] << 8) |
+               ((uint32_t)lt[(wv[k] >> 16) & 0xff] << 16) | ((uint32_t)lt[wv[k] >> 24] << 24);
+      reinterpret_cast<uint4*>(q + (int64_t)r * K + kb * 128)[cc & 7] = make_uint4(o[0], o[1], o[2], o[3]);
+      if (WRITE_BF16) {
+        const uint16_t* lb = lutb[tile];
+        uint32_t h[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          h[2 * k] = (uint32_t)lb[wv[k] & 0xff] | ((uint32_t)lb[(wv[k] >> 8) & 0xff] << 16);
+          h[2 * k + 1] = (uint32_t)lb[(wv[k] >> 16) & 0xff] | ((uint32_t)lb[wv[k] >> 24] << 16);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(wbf + (int64_t)r * K + kb * 128) + 2 * (cc & 7);
+        dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+      }
+    }
+  }
 }
 
 template <int FMT>
@@ -353,7 +403,8 @@ hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int8_t
 
 hipError_t launch_requant_block(const uint8_t* w, const float* si, int64_t N, int64_t K, int8_t* q, float* s,
                                 uint16_t* wbf, hipStream_t st) {
-  dim3 grid((unsigned)((K >> 7) * ((N + 127) >> 7)));
+  const int64_t NS = ((K >> 7) + kStripTiles - 1) / kStripTiles;
+  dim3 grid((unsigned)(NS * ((N + 127) >> 7)));
   const uint4* wp = reinterpret_cast<const uint4*>(w);
   if (wbf)
     hipLaunchKernelGGL((k_requant_tile_fp8<true>), grid, dim3(256), 0, st, wp, si, q, s, wbf, (int)N, (int)K);
