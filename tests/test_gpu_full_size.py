@@ -1,4 +1,4 @@
-"""GPU parity of the large-M GEMMs at the benchmark's full sizes, on samples.
+"""GPU parity of the GEMMs at the benchmark's full sizes, on samples.
 
 The DeepSeek-V3 dense MLP at 4096 tokens: gate_up (K = 7168 -> N = 36864)
 and down (K = 18432 -> N = 7168), channel-wise (the headline step) and
@@ -13,6 +13,8 @@ its scales), so the oracle's GEMM over 64 sampled rows (the first and last
 among them) times three whole 128-column weight blocks (the first, the last
 and one drawn at random) equals that part of the full product.
 
+The decode, W8A16 and MoE rows follow below with the same sampling.
+
 Bars as in test_gpu_gemm: channel-wise int32 accumulator and fp32 output
 bit-exact; block-wise fp32 within 1e-5 normwise of the oracle's fp32 path
 (1e-2 of its fp64 path); bf16 outputs the round-to-nearest-even of the
@@ -25,7 +27,7 @@ import torch
 
 import synth
 import w8a8_int8_quantized_amd as w8
-from oracle import formats, gemm, quant
+from oracle import formats, gemm, quant, routing
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -95,3 +97,93 @@ def test_block_full_size_sampled(name):
     gotb = _pick(yb.view(torch.int16), rows, cols).view(np.uint16)
     assert np.array_equal(gotb, formats.f32_to_bf16_bits(got32))
     assert gemm.normwise_rel_err(formats.bf16_bits_to_f32(gotb).astype(np.float64), y64) <= 1e-2
+
+
+# ------------------------------------------------------------ decode shapes
+# Block-wise decode at the benchmark's decode rows (K = 7168 -> N = 36864,
+# M in {1, 8, 32, 64}: one weight-streaming launch per M), every row checked
+# on three whole 128-column blocks.
+def test_block_decode_full_size_sampled():
+    K, N = SHAPES["gate_up"]
+    qw, sw = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=52)))
+    _, blocks, cols = _sample(N, seed=53)
+    W, SW = (torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (qw, sw))
+    qwc, swb = qw[cols], sw[blocks]
+    del qw
+    for M in (1, 8, 32, 64):
+        print(f"block decode: M={M} K={K} N={N}", flush=True)
+        qa, sa = quant.quant_act_group(synth.to_numpy(synth.activations(M, K, seed=50 + M)))
+        _, y64, y32 = gemm.gemm_block(qa, sa, qwc, swb)
+        A, SA = (torch.from_numpy(a).to(DEV) for a in (qa, sa))
+        rows = np.arange(M)
+        got32 = _pick(w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32), rows, cols)
+        e32, e64 = gemm.normwise_rel_err(got32, y32), gemm.normwise_rel_err(got32, y64)
+        assert e32 <= 1e-5 and e64 <= 1e-2, (M, e32, e64)
+        gotb = _pick(w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.bfloat16).view(torch.int16), rows, cols)
+        assert np.array_equal(gotb.view(np.uint16), formats.f32_to_bf16_bits(got32))
+
+
+# W8A16 at the benchmark's Qwen3-8B-shaped rows (qkv K = 4096 -> N = 12288,
+# down K = 12288 -> N = 4096; fp16 activations, group-wise INT8 weights).
+@pytest.mark.parametrize("name,K,N", [("qkv", 4096, 12288), ("down", 12288, 4096)])
+def test_w8a16_full_size_sampled(name, K, N):
+    qw, sw = quant.quant_act_group(synth.weights(N, K, seed=62, dtype=torch.float16).numpy())
+    _, _, cols = _sample(N, seed=63)
+    W, SW = (torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (qw, sw))
+    qwc, swc = qw[cols], sw[cols]
+    for M in (1, 8, 32, 64):
+        print(f"w8a16 {name}: M={M} K={K} N={N}", flush=True)
+        x = synth.activations(M, K, seed=60 + M, dtype=torch.float16).numpy()
+        y64, y32 = gemm.gemm_w8a16_group(x, qwc, swc)
+        got = _pick(w8.gemm_w8a16_group(torch.from_numpy(x).to(DEV), W, SW), np.arange(M), cols).astype(np.float32)
+        e32, e64 = gemm.normwise_rel_err(got, y32), gemm.normwise_rel_err(got, y64)
+        assert e32 <= 1e-3 and e64 <= 1e-2, (M, e32, e64)
+
+
+# ---------------------------------------------------------------------- MoE
+# The benchmark's MoE gate_up: 256 experts, top-8 routing of 4096 tokens
+# (32768 expert-sorted rows, 128 per expert on average), K = 7168 -> N = 4096
+# per expert, 7.5 GB of expert weights.  Four experts are checked (the first,
+# the last, the one with the most rows and the one with the fewest non-zero
+# rows), on three whole 128-column blocks: their weights and every
+# activation row come from the oracle's quantisers; the other experts'
+# weights are arbitrary INT8 codes (torch's generator), which no checked
+# output depends on.
+def test_moe_full_size_sampled():
+    E, T, TOPK = 256, 4096, 8
+    K, N = 7168, 4096
+    NB, KB = N // 128, K // 128
+    rows, _, offs = routing.topk_route(synth.router_logits(T, E, seed=4).numpy(), TOPK)
+    P = rows.size
+    x = synth.to_numpy(synth.activations(T, K, seed=71))
+    qa, sa = quant.quant_act_group(x[rows])
+    del x
+    cnt = np.diff(offs)
+    nz = np.nonzero(cnt)[0]
+    experts = sorted({0, E - 1, int(np.argmax(cnt)), int(nz[np.argmin(cnt[nz])])})
+    print(f"moe: E={E} P={P} K={K} N={N} experts {experts} rows {[int(cnt[e]) for e in experts]}", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(72)
+    Wq = torch.empty(E, N, K, dtype=torch.int8, device=DEV)
+    for e0 in range(0, E, 16):
+        Wq[e0:e0 + 16] = torch.randint(-127, 128, (16, N, K), generator=g, dtype=torch.int8, device=DEV)
+    Ws = torch.rand(E, NB, KB, generator=g, device=DEV) * 1e-3 + 1e-4
+    ref = {}
+    for e in experts:
+        qw, sw = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=200 + e)))
+        Wq[e] = torch.from_numpy(qw).to(DEV)
+        Ws[e] = torch.from_numpy(sw).to(DEV)
+        ref[e] = (qw, sw)
+    _, blocks, cols = _sample(N, seed=73)
+    A, SA = (torch.from_numpy(a).to(DEV) for a in (qa, sa))
+    OFF = torch.from_numpy(offs.astype(np.int32)).to(DEV)
+    y = w8.gemm_w8a8_block_grouped(A, SA, Wq, Ws, OFF, out_dtype=torch.float32)
+    yb = w8.gemm_w8a8_block_grouped(A, SA, Wq, Ws, OFF, out_dtype=torch.bfloat16)
+    for e in experts:
+        r = np.arange(offs[e], offs[e + 1])
+        qw, sw = ref[e]
+        _, y64, y32 = gemm.gemm_block(qa[r], sa[r], qw[cols], sw[blocks])
+        got32 = _pick(y, r, cols)
+        e32, e64 = gemm.normwise_rel_err(got32, y32), gemm.normwise_rel_err(got32, y64)
+        assert e32 <= 1e-5 and e64 <= 1e-2, (e, e32, e64)
+        assert np.array_equal(_pick(yb.view(torch.int16), r, cols).view(np.uint16), formats.f32_to_bf16_bits(got32))
