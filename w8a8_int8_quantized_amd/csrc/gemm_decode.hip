@@ -996,7 +996,8 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s,
   // kernel's per-wave activation loads), else the decode kernel; more rows
   // the shared-activation kernel.  Its width comes from the balance rule (4
   // waves where no width balances), K is split over S workgroups until there
-  // are two per CU (slices of at least 4 K blocks), the ring depth follows the
+  // are two per CU below 32 rows and one from there (slices of at least 4 K
+  // blocks), the ring depth follows the
   // waves per CU, and the slices' fp32 partials go to the split-K workspace
   // and are summed in order.
   const int nwv0 = pick_shared_width(N);
@@ -1005,7 +1006,10 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s,
   const int64_t wgs1 = (N + 16 * nwv - 1) / (16 * nwv);
   const int64_t KBt = K >> 7;
   int S = 1;
-  while (wgs1 * S < 2 * kCUs && S < 8 && KBt / (2 * S) >= 4) S *= 2;
+  // (from 32 rows one workgroup per CU: the slices' partials and their
+  // reduction then cost more than the second workgroup's latency hiding)
+  const int64_t target = M >= 32 ? kCUs : 2 * kCUs;
+  while (wgs1 * S < target && S < 8 && KBt / (2 * S) >= 4) S *= 2;
   const int64_t wpc = nwv * ((wgs1 * S + kCUs - 1) / kCUs);
   const int pf = wpc <= 4 ? 8 : (wpc <= 8 ? 4 : 2);
   float* part = nullptr;
