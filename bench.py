@@ -222,6 +222,11 @@ def rows(args):
             ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wsets[i][0], wsets[i][1], out=y), 4, R)
             e = gemm_entry(ms, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
             out[f"decode_block_m{M}"] = e
+            # the one-call linear layer: bf16 activations quantised online, then the same GEMM
+            xb = synth.activations(M, K, seed=M, device=dev)
+            wsp = torch.empty(w8.linear_workspace_bytes(w8.W8_SCHEME_BLOCK, M, K), dtype=torch.uint8, device=dev)
+            ms = time_calls(lambda i: w8.linear_w8a8_block(xb, wsets[i][0], wsets[i][1], out=y, workspace=wsp), 4, R)
+            out[f"decode_linear_block_m{M}"] = gemm_entry(ms, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
         del wsets
         torch.cuda.empty_cache()
 

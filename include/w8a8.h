@@ -13,9 +13,9 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  Calls
  *     are thread-safe.  The only state the library keeps is a split-K
- *     workspace per (device, stream) for gemm_w8a8_block, gemm_w8a8_channel
- *     and gemm_w8a16_group (described at gemm_w8a8_block); every other entry
- *     point allocates nothing.
+ *     workspace per (device, stream) for gemm_w8a8_block, gemm_w8a8_channel,
+ *     gemm_w8a16_group and the linear_* calls (described at
+ *     gemm_w8a8_block); every other entry point allocates nothing.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream) and returns without synchronising.
  *     Results are visible once the stream reaches that point.
@@ -49,7 +49,8 @@ enum w8_status {
   W8_ERR_SHAPE = -2,  /* negative size, K % 128 != 0, or a size beyond the limits below */
   W8_ERR_ALIGN = -3,  /* a pointer is not aligned as required */
   W8_ERR_DTYPE = -4,  /* unsupported dtype code */
-  W8_ERR_LAUNCH = -5  /* the HIP runtime rejected a kernel launch or a workspace allocation */
+  W8_ERR_LAUNCH = -5, /* the HIP runtime rejected a kernel launch or a workspace allocation */
+  W8_ERR_WORKSPACE = -6 /* a caller-provided workspace is smaller than required */
 };
 
 enum w8_dtype { W8_BF16 = 0, W8_FP16 = 1, W8_FP32 = 2, W8_I32 = 3 };
@@ -200,6 +201,45 @@ int gemm_w8a8_block_grouped(const int8_t* A, const float* a_scale,
                             const int32_t* expert_offsets, void* Y, int y_dtype,
                             int64_t E, int64_t P, int64_t N, int64_t K,
                             void* stream);
+
+/*
+ * One-call linear layers (page 1 section 2.3: activations are quantised
+ * online, per token group for the block-wise scheme and per token for the
+ * channel-wise one, then multiplied by the offline-quantised weights):
+ *   linear_w8a8_block   = quant_act_group(x) then gemm_w8a8_block
+ *   linear_w8a8_channel = quant_act_token(x) then gemm_w8a8_channel
+ * on `stream`, with the same kernels, so Y is bit-identical to the two calls
+ * made separately.
+ *   x [M][K] bf16 (x_dtype W8_BF16) or fp16 (W8_FP16); W, w_scale as for the
+ *   GEMM; Y [M][N] bf16 or fp32 (y_dtype).
+ *   workspace: caller-owned device memory of at least
+ *   linear_workspace_bytes(scheme, M, K) bytes (workspace_bytes says how
+ *   many it holds; fewer gives W8_ERR_WORKSPACE), 256-byte aligned.  It takes
+ *   the int8 codes of x ([M][K] at offset 0) and their fp32 scales (at offset
+ *   M*K rounded up to 256: [M][KB] for the block-wise scheme, [M] for the
+ *   channel-wise one); it must not be used by other work until the stream
+ *   has passed this call, and must not overlap x, W, w_scale or Y.  The
+ *   GEMM may use the split-K workspace described at gemm_w8a8_block.
+ *   Channel-wise: K <= 2^17, as for gemm_w8a8_channel.
+ * Argument errors return with nothing enqueued; W8_ERR_LAUNCH may leave the
+ * quantisation (which writes only the workspace) enqueued.
+ */
+enum w8_scheme { W8_SCHEME_BLOCK = 0, W8_SCHEME_CHANNEL = 1 };
+
+/* Workspace bytes for linear_w8a8_block (scheme W8_SCHEME_BLOCK) or
+   linear_w8a8_channel (W8_SCHEME_CHANNEL) over M x K activations; a negative
+   w8_status for an unknown scheme or a shape the linear calls reject. */
+int64_t linear_workspace_bytes(int scheme, int64_t M, int64_t K);
+
+int linear_w8a8_block(const void* x, int x_dtype, const int8_t* W,
+                      const float* w_scale, void* Y, int y_dtype,
+                      int64_t M, int64_t N, int64_t K, void* workspace,
+                      int64_t workspace_bytes, void* stream);
+
+int linear_w8a8_channel(const void* x, int x_dtype, const int8_t* W,
+                        const float* w_scale, void* Y, int y_dtype,
+                        int64_t M, int64_t N, int64_t K, void* workspace,
+                        int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

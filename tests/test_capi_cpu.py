@@ -13,7 +13,7 @@ import w8a8_int8_quantized_amd as w8
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w8a8.h")
 
-OK, ENULL, ESHAPE, EALIGN, EDTYPE = 0, -1, -2, -3, -4
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS = 0, -1, -2, -3, -4, -6
 P16 = ctypes.c_void_p(1 << 20)        # a 16-byte aligned fake address (never dereferenced)
 P4 = ctypes.c_void_p((1 << 20) + 4)   # 4-byte but not 16-byte aligned
 NUL = ctypes.c_void_p(0)
@@ -22,7 +22,7 @@ NUL = ctypes.c_void_p(0)
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"^(?:int|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M))
+    return set(re.findall(r"^(?:int|int64_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M))
 
 
 def test_every_declared_symbol_is_exported():
@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     assert w8.lib.w8_abi_version() == 1
-    for rc in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, -5):
+    for rc in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, -5, EWS):
         assert len(w8.lib.w8_status_string(rc)) > 0
     assert w8.lib.w8_status_string(99) == b"unknown status"
 
@@ -88,6 +88,47 @@ def test_gemm_argument_checks():
     assert L.gemm_w8a8_block_grouped(P16, P16, P16, P16, NUL, P16, w8.W8_BF16, 8, 4, 4, 128, NUL) == ENULL
     assert L.gemm_w8a8_block_grouped(P16, P16, P16, P16, P16, P16, w8.W8_I32, 8, 4, 4, 128, NUL) == EDTYPE
     assert L.gemm_w8a8_block_grouped(NUL, NUL, NUL, NUL, NUL, NUL, w8.W8_BF16, 8, 0, 4, 128, NUL) == OK
+
+
+def test_linear_workspace_bytes():
+    L = w8.lib
+    B, C = w8.W8_SCHEME_BLOCK, w8.W8_SCHEME_CHANNEL
+    # int8 codes rounded up to 256 bytes, then fp32 scales: M x K/128 (block) or M (channel)
+    assert L.linear_workspace_bytes(B, 3, 256) == 768 + 3 * 2 * 4
+    assert L.linear_workspace_bytes(C, 3, 256) == 768 + 3 * 4
+    assert L.linear_workspace_bytes(B, 1, 128) == 256 + 4
+    assert L.linear_workspace_bytes(C, 5, 128) == 768 + 5 * 4
+    assert L.linear_workspace_bytes(B, 4096, 7168) == 4096 * 7168 + 4096 * 56 * 4
+    assert L.linear_workspace_bytes(B, 0, 128) == 0
+    assert L.linear_workspace_bytes(2, 4, 128) == EDTYPE
+    assert L.linear_workspace_bytes(B, 4, 100) == ESHAPE
+    assert L.linear_workspace_bytes(C, -1, 128) == ESHAPE
+
+
+def test_linear_argument_checks():
+    L = w8.lib
+    big = 1 << 30
+    P256 = ctypes.c_void_p(1 << 20)
+    P16o = ctypes.c_void_p((1 << 20) + 16)   # 16-byte but not 256-byte aligned
+    for fn in (L.linear_w8a8_block, L.linear_w8a8_channel):
+        assert fn(P16, w8.W8_FP32, P16, P16, P16, w8.W8_BF16, 4, 4, 128, P256, big, NUL) == EDTYPE
+        assert fn(P16, 0, P16, P16, P16, w8.W8_I32, 4, 4, 128, P256, big, NUL) == EDTYPE
+        assert fn(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 100, P256, big, NUL) == ESHAPE
+        assert fn(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 0, P256, big, NUL) == ESHAPE
+        assert fn(NUL, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 128, P256, big, NUL) == ENULL
+        assert fn(P16, 0, P16, NUL, P16, w8.W8_BF16, 4, 4, 128, P256, big, NUL) == ENULL
+        assert fn(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 128, NUL, big, NUL) == ENULL
+        assert fn(P4, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 128, P256, big, NUL) == EALIGN
+        assert fn(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 128, P16o, big, NUL) == EALIGN
+        assert fn(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 128, P256, 256, NUL) == EWS
+        assert fn(NUL, 0, NUL, NUL, NUL, w8.W8_BF16, 0, 4, 128, NUL, 0, NUL) == OK     # M == 0: no-op
+        assert fn(NUL, 0, NUL, NUL, NUL, w8.W8_BF16, 4, 0, 128, NUL, 0, NUL) == OK     # N == 0: no-op
+    # the channel-wise GEMM's K limit
+    assert L.linear_w8a8_channel(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 1 << 18, P256, 1 << 40, NUL) == ESHAPE
+    # one byte short of the required size
+    need = L.linear_workspace_bytes(w8.W8_SCHEME_BLOCK, 4, 128)
+    assert need == 512 + 16
+    assert L.linear_w8a8_block(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 128, P256, need - 1, NUL) == EWS
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -11,6 +11,7 @@ fallback: if libw8a8.so is missing, importing this package raises.
     wq, ws = requant_fp8_to_int8_block(w_fp8, scale_inv)
     y = gemm_w8a8_block(q, s, wq, ws)          # bf16 (or fp32) output
     y = gemm_w8a8_channel(q, s, wq, ws)
+    y = linear_w8a8_block(x, wq, ws)           # quant_act_group + gemm_w8a8_block in one call
 """
 
 import ctypes
@@ -22,6 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw8a8.so")
 
 W8_BF16, W8_FP16, W8_FP32, W8_I32 = 0, 1, 2, 3
+W8_SCHEME_BLOCK, W8_SCHEME_CHANNEL = 0, 1
 GROUP = 128
 
 _FUNCS = {
@@ -53,6 +55,13 @@ _FUNCS = {
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_void_p]),
+    "linear_workspace_bytes": (ctypes.c_int64, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]),
+    "linear_w8a8_block": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "linear_w8a8_channel": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
 }
 
 
@@ -232,3 +241,33 @@ def gemm_w8a8_block_grouped(A, a_scale, W, w_scale, expert_offsets, out_dtype=to
     _check(lib.gemm_w8a8_block_grouped(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(expert_offsets), _p(y),
                                        _out_code(y.dtype), E, P, N, K, _stream()), "gemm_w8a8_block_grouped")
     return y
+
+
+# ------------------------------------------------------------- linear layers
+def linear_workspace_bytes(scheme, M, K):
+    """Bytes of workspace linear_w8a8_block (W8_SCHEME_BLOCK) or linear_w8a8_channel needs."""
+    n = lib.linear_workspace_bytes(scheme, M, K)
+    _check(min(n, 0), "linear_workspace_bytes")
+    return n
+
+
+def _linear(fn, scheme, x, W, w_scale, out_dtype, out, workspace):
+    _dev(x, W, w_scale, out, workspace)
+    M, K = x.shape
+    N = W.shape[0]
+    need = linear_workspace_bytes(scheme, M, K)
+    ws = workspace if workspace is not None else _empty((max(need, 1),), torch.uint8, x)
+    y = out if out is not None else _empty((M, N), out_dtype, x)
+    _check(fn(_p(x), _act_dtype(x), _p(W), _p(w_scale), _p(y), _out_code(y.dtype), M, N, K, _p(ws),
+              ws.numel() * ws.element_size(), _stream()), fn.__name__)
+    return y
+
+
+def linear_w8a8_block(x, W, w_scale, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """quant_act_group(x) then the block-wise GEMM, in one call; x [M, K] bf16/fp16."""
+    return _linear(lib.linear_w8a8_block, W8_SCHEME_BLOCK, x, W, w_scale, out_dtype, out, workspace)
+
+
+def linear_w8a8_channel(x, W, w_scale, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """quant_act_token(x) then the channel-wise GEMM, in one call; x [M, K] bf16/fp16."""
+    return _linear(lib.linear_w8a8_channel, W8_SCHEME_CHANNEL, x, W, w_scale, out_dtype, out, workspace)

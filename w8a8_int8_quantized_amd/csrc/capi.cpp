@@ -66,6 +66,7 @@ const char* w8_status_string(int status) {
     case W8_ERR_ALIGN: return "misaligned pointer (data 16-byte, scales 4-byte)";
     case W8_ERR_DTYPE: return "unsupported dtype";
     case W8_ERR_LAUNCH: return "kernel launch or workspace allocation failed";
+    case W8_ERR_WORKSPACE: return "caller-provided workspace too small";
     default: return "unknown status";
   }
 }
@@ -188,6 +189,50 @@ int gemm_w8a8_block_grouped(const int8_t* A, const float* a_scale, const int8_t*
   if (!aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(expert_offsets, 4)) return W8_ERR_ALIGN;
   return status_of(w8::launch_gemm_block_grouped(A, a_scale, W, w_scale, expert_offsets, Y, out, E, P, N, K,
                                                  as_stream(stream)));
+}
+
+int64_t linear_workspace_bytes(int scheme, int64_t M, int64_t K) {
+  if (scheme != W8_SCHEME_BLOCK && scheme != W8_SCHEME_CHANNEL) return W8_ERR_DTYPE;
+  int rc = check_rows_k(M, K);
+  if (rc) return rc;
+  const int64_t codes = (M * K + 255) / 256 * 256;
+  return codes + 4 * (scheme == W8_SCHEME_BLOCK ? M * (K / 128) : M);
+}
+
+static int linear_common(bool block, const void* x, int x_dtype, const int8_t* W, const float* w_scale, void* Y,
+                         int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
+  if (x_dtype != W8_BF16 && x_dtype != W8_FP16) return W8_ERR_DTYPE;
+  w8::OutKind out;
+  int rc = check_out(y_dtype, false, &out);
+  if (rc) return rc;
+  // x takes the place of A in the shape, null and 16-byte alignment checks
+  rc = check_gemm_common(static_cast<const int8_t*>(x), W, Y, M, N, K);
+  if (rc || M == 0 || N == 0) return rc;
+  if (K == 0 || (!block && K > (int64_t(1) << 17))) return W8_ERR_SHAPE;
+  if (!w_scale || !workspace) return W8_ERR_NULL;
+  if (!aligned(w_scale, 4) || !aligned(workspace, 256)) return W8_ERR_ALIGN;
+  const int64_t need = linear_workspace_bytes(block ? W8_SCHEME_BLOCK : W8_SCHEME_CHANNEL, M, K);
+  if (workspace_bytes < need) return W8_ERR_WORKSPACE;
+  int8_t* q = static_cast<int8_t*>(workspace);
+  float* s = reinterpret_cast<float*>(static_cast<char*>(workspace) + (M * K + 255) / 256 * 256);
+  const hipStream_t st = as_stream(stream);
+  const bool fp16 = x_dtype == W8_FP16;
+  const hipError_t e =
+      block ? w8::launch_quant_group(x, fp16, M, K, q, s, st) : w8::launch_quant_token(x, fp16, M, K, q, s, st);
+  if (e != hipSuccess) return W8_ERR_LAUNCH;
+  return status_of(block ? w8::launch_gemm_block(q, s, W, w_scale, Y, out, M, N, K, st)
+                         : w8::launch_gemm_channel(q, s, W, w_scale, Y, out, M, N, K, st));
+}
+
+int linear_w8a8_block(const void* x, int x_dtype, const int8_t* W, const float* w_scale, void* Y, int y_dtype,
+                      int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+  return linear_common(true, x, x_dtype, W, w_scale, Y, y_dtype, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int linear_w8a8_channel(const void* x, int x_dtype, const int8_t* W, const float* w_scale, void* Y, int y_dtype,
+                        int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+  return linear_common(false, x, x_dtype, W, w_scale, Y, y_dtype, M, N, K, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
