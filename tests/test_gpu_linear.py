@@ -3,12 +3,13 @@ then the INT8 GEMM; page "DeepSeek R1 INT8 quantisation in SGLang",
 section 2.3).
 
 linear_w8a8_block / linear_w8a8_channel against the oracle's quantiser
-followed by its GEMM: the int8 codes and fp32 scales the call leaves in the
-workspace bit-exact, the output within the GEMM bars of test_gpu_gemm
+followed by its GEMM: the output within the GEMM bars of test_gpu_gemm
 (channel-wise fp32 bit-exact, block-wise fp32 within 1e-5 normwise of the
 oracle's fp32 path, both within 1e-2 of its fp64 path), and bit-identical to
-the quantiser and GEMM entry points called one after the other.  One
-workspace serves two calls in a row, the second on a smaller input.
+the quantiser and GEMM entry points called one after the other; the int8
+codes and fp32 scales left in the workspace bit-exact to the oracle's
+quantiser.  One workspace serves two calls in a row, the second on a smaller
+input.
 """
 
 import numpy as np
@@ -25,17 +26,13 @@ DEV = "cuda"
 # (M, N, K): decode rows (weight-streaming kernels), a split-K tile grid and
 # ragged 128/256-row tiles; N ragged against the 128-column weight blocks.
 CASES = [(1, 300, 256), (37, 700, 1024), (130, 513, 640), (300, 1100, 384)]
+# decode rows on output widths that spread evenly over the CUs (the
+# shared-activation weight-streaming kernel), odd numbers of K blocks
+WIDE = [(1, 36864, 640), (5, 12288, 384), (16, 36864, 1152), (11, 12288, 128), (17, 12288, 384)]
 
 
 def _np(t):
     return t.detach().cpu().numpy()
-
-
-def _inputs(M, N, K, seed, fp16):
-    dt = torch.float16 if fp16 else torch.bfloat16
-    x = synth.activations(M, K, seed=seed, dtype=dt)
-    w = synth.to_numpy(synth.weights(N, K, seed=seed + 1))
-    return x, (x.numpy() if fp16 else synth.to_numpy(x)), w
 
 
 def _workspace_parts(ws, scheme, M, K):
@@ -46,8 +43,15 @@ def _workspace_parts(ws, scheme, M, K):
     return q, s
 
 
+def _inputs(M, N, K, seed, fp16):
+    dt = torch.float16 if fp16 else torch.bfloat16
+    x = synth.activations(M, K, seed=seed, dtype=dt)
+    w = synth.to_numpy(synth.weights(N, K, seed=seed + 1))
+    return x, (x.numpy() if fp16 else synth.to_numpy(x)), w
+
+
 @pytest.mark.parametrize("fp16", [False, True])
-@pytest.mark.parametrize("M,N,K", CASES)
+@pytest.mark.parametrize("M,N,K", CASES + WIDE)
 def test_linear_block(M, N, K, fp16):
     print(f"linear block M={M} N={N} K={K} fp16={fp16}", flush=True)
     x, xo, w = _inputs(M, N, K, seed=M + 11, fp16=fp16)
@@ -93,9 +97,36 @@ def test_linear_channel(M, N, K, fp16):
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), formats.f32_to_bf16_bits(y32))
 
 
+@pytest.mark.parametrize("fp16", [False, True])
+def test_linear_block_zero_and_extreme_groups(fp16):
+    """Zero rows and groups (the 1e-10 floor), a group whose amax sits at
+    both signs, and values of very different magnitude in one row (8 rows,
+    N = 12288), bit-identical to the quantiser and GEMM called one after
+    the other."""
+    M, N, K = 8, 12288, 512
+    x, _, w = _inputs(M, N, K, seed=77, fp16=fp16)
+    x[3] = 0
+    x[5, 128:256] = 0
+    x[6, 0:128] = torch.linspace(-3.0, 3.0, 128).to(x.dtype)
+    x[7, 256:384] *= 1000
+    xo = x.numpy() if fp16 else synth.to_numpy(x)
+    qa, sa = quant.quant_act_group(xo)
+    qw, sw = quant.quant_weight_block(w)
+    _, y64, y32 = gemm.gemm_block(qa, sa, qw, sw)
+    X = x.to(DEV)
+    W, SW = (torch.from_numpy(a).to(DEV) for a in (qw, sw))
+    got = _np(w8.linear_w8a8_block(X, W, SW, out_dtype=torch.float32))
+    q2, s2 = w8.quant_act_group(X)
+    ref = _np(w8.gemm_w8a8_block(q2, s2, W, SW, out_dtype=torch.float32))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert not got[3].any() and np.isfinite(got).all()
+    e32 = gemm.normwise_rel_err(got, y32)
+    assert e32 <= 1e-5, e32
+
+
 def test_linear_workspace_reused_smaller():
     """One workspace, two calls in a row; the second input is smaller."""
-    K, N = 512, 400
+    K, N = 512, 12288
     ws = torch.empty(w8.linear_workspace_bytes(w8.W8_SCHEME_BLOCK, 200, K), dtype=torch.uint8, device=DEV)
     for M in (200, 9):
         print(f"linear reuse M={M}", flush=True)
