@@ -230,6 +230,29 @@ def rows(args):
         del wsets
         torch.cuda.empty_cache()
 
+    if want("asym"):
+        # --- asymmetric per-tensor activations: quantiser (two passes over x;
+        # algorithmic bytes 2 in + 1 out per element) and the GEMM at 4096 rows
+        # and one row, gate_up shape, per-channel weights
+        K, N = GATE_UP
+        x = synth.activations(4096, K, seed=7, device=dev)
+        ms = time_calls(lambda i: w8.quant_act_asym(x), 1, R)
+        b = 4096 * K * 3
+        out["quant_act_asym_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                           "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+        qa, prm = w8.quant_act_asym(x)
+        wq, wsc = w8.quant_act_token(synth.weights(N, K, seed=8, device=dev))
+        wsum = w8.weight_row_sums(wq)
+        y = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: w8.gemm_w8a8_asym(qa, prm, wq, wsc, wsum, out=y), 1, max(5, R // 2))
+        out["gemm_asym_m4096_gate_up"] = gemm_entry(ms, 4096, N, K, N * K)
+        y1 = torch.empty(1, N, dtype=torch.bfloat16, device=dev)
+        a1 = qa[:1].contiguous()
+        ms = time_calls(lambda i: w8.gemm_w8a8_asym(a1, prm, wq, wsc, wsum, out=y1), 1, R)
+        out["decode_asym_m1_gate_up"] = gemm_entry(ms, 1, N, K, N * K + 8 * N)
+        del x, qa, wq, y
+        torch.cuda.empty_cache()
+
     if want("w8a16"):
         # --- decode W8A16: Qwen3-8B-shaped linears, 20 weight copies (> 1 GB)
         for name in ("w8a16_qkv", "w8a16_down"):

@@ -15,7 +15,8 @@
  *     are thread-safe.  The only state the library keeps is a split-K
  *     workspace per (device, stream) for gemm_w8a8_block, gemm_w8a8_channel,
  *     gemm_w8a16_group and the linear_* calls (described at
- *     gemm_w8a8_block); every other entry point allocates nothing.
+ *     gemm_w8a8_block), and one for quant_act_asym and gemm_w8a8_asym;
+ *     every other entry point allocates nothing.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream) and returns without synchronising.
  *     Results are visible once the stream reaches that point.
@@ -240,6 +241,47 @@ int linear_w8a8_channel(const void* x, int x_dtype, const int8_t* W,
                         const float* w_scale, void* Y, int y_dtype,
                         int64_t M, int64_t N, int64_t K, void* workspace,
                         int64_t workspace_bytes, void* stream);
+
+/*
+ * Asymmetric per-tensor activation quantisation, an alternative beside the
+ * symmetric scheme above (page 2, Meituan INT8 DeepSeek R1 practice guide,
+ * part two, item 1, dynamic range-aware quantisation).  Over the whole
+ * M x K tensor, in fp32 IEEE operations:
+ *   mn, mx = min(x), max(x)
+ *   s = max(mx - mn, 1e-10) / 255,  z = -mn / s   (z is not rounded)
+ *   q = clamp(round_half_even((x - mn) / s), 0, 255)
+ *   x [M][K] bf16 or fp16 (x_dtype); q_shifted [M][K] int8 out, holding
+ *   q - 128 (the byte q ^ 0x80), which the int8 GEMM takes directly;
+ *   params [2] fp32 DEVICE out: {s, z}.
+ * Two kernel launches; their per-workgroup partial ranges (at most 8 KB) go
+ * to a library workspace per (device, stream) like the split-K one (slot of
+ * its own).  M * K == 0 is a no-op (params untouched).
+ */
+int quant_act_asym(const void* x, int x_dtype, int64_t M, int64_t K,
+                   int8_t* q_shifted, float* params, void* stream);
+
+/* WS[n] = sum_k W[n][k] (exact int32) of int8 weights W [N][K], for
+   gemm_w8a8_asym.  0 < K <= 2^16 (N == 0 is a no-op). */
+int weight_row_sums(const int8_t* W, int64_t N, int64_t K, int32_t* w_sum,
+                    void* stream);
+
+/*
+ * GEMM of asymmetric activations (quant_act_asym) with symmetric
+ * per-channel int8 weights (quant_act_token applied to W, page 1 section
+ * 2.3 channel-wise scheme):
+ *   ACC[m][n] = sum_k q[m][k] W[n][k]   (exact; q = stored code + 128)
+ *   Y[m][n]   = fp32(fp32(s * w_scale[n]) * fp32(fp32(ACC) - fp32(z * fp32(w_sum[n]))))
+ *   A_shifted [M][K] int8, a_params [2] {s, z} DEVICE, W [N][K] int8,
+ *   w_scale [N], w_sum [N] int32 (weight_row_sums), Y [M][N] bf16 or fp32.
+ * K <= 2^16 (ACC stays inside int32).  The stored codes' int32 products
+ * (the channel-wise GEMM) go to a library workspace of M x N x 4 bytes per
+ * (device, stream), grown on demand like the split-K one, then one epilogue
+ * launch forms Y.
+ */
+int gemm_w8a8_asym(const int8_t* A_shifted, const float* a_params,
+                   const int8_t* W, const float* w_scale,
+                   const int32_t* w_sum, void* Y, int y_dtype,
+                   int64_t M, int64_t N, int64_t K, void* stream);
 
 #ifdef __cplusplus
 }

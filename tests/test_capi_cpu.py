@@ -131,6 +131,25 @@ def test_linear_argument_checks():
     assert L.linear_w8a8_block(P16, 0, P16, P16, P16, w8.W8_BF16, 4, 4, 128, P256, need - 1, NUL) == EWS
 
 
+def test_asym_argument_checks():
+    L = w8.lib
+    assert L.quant_act_asym(P16, w8.W8_FP32, 4, 128, P16, P16, NUL) == EDTYPE
+    assert L.quant_act_asym(P16, 0, 4, 100, P16, P16, NUL) == ESHAPE
+    assert L.quant_act_asym(P16, 0, 4, 128, P16, NUL, NUL) == ENULL
+    assert L.quant_act_asym(P4, 0, 4, 128, P16, P16, NUL) == EALIGN
+    assert L.quant_act_asym(NUL, 0, 0, 128, NUL, NUL, NUL) == OK
+    assert L.weight_row_sums(P16, 4, 1 << 17, P16, NUL) == ESHAPE          # K beyond 2^16
+    assert L.weight_row_sums(P16, 4, 0, P16, NUL) == ESHAPE
+    assert L.weight_row_sums(P16, 4, 128, NUL, NUL) == ENULL
+    assert L.weight_row_sums(NUL, 0, 128, NUL, NUL) == OK
+    assert L.gemm_w8a8_asym(P16, P16, P16, P16, P16, P16, w8.W8_I32, 4, 4, 128, NUL) == EDTYPE
+    assert L.gemm_w8a8_asym(P16, P16, P16, P16, P16, P16, w8.W8_BF16, 4, 4, 1 << 17, NUL) == ESHAPE
+    assert L.gemm_w8a8_asym(P16, NUL, P16, P16, P16, P16, w8.W8_BF16, 4, 4, 128, NUL) == ENULL
+    assert L.gemm_w8a8_asym(P16, P16, P16, P16, NUL, P16, w8.W8_BF16, 4, 4, 128, NUL) == ENULL
+    assert L.gemm_w8a8_asym(P4, P16, P16, P16, P16, P16, w8.W8_FP32, 4, 4, 128, NUL) == EALIGN   # misaligned A
+    assert L.gemm_w8a8_asym(NUL, NUL, NUL, NUL, NUL, NUL, w8.W8_BF16, 0, 4, 128, NUL) == OK
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros(4, 128, dtype=torch.bfloat16)

@@ -56,6 +56,13 @@ _FUNCS = {
                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_void_p]),
     "linear_workspace_bytes": (ctypes.c_int64, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]),
+    "quant_act_asym": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "weight_row_sums": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_void_p]),
+    "gemm_w8a8_asym": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "linear_w8a8_block": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
@@ -271,3 +278,37 @@ def linear_w8a8_block(x, W, w_scale, out_dtype=torch.bfloat16, out=None, workspa
 def linear_w8a8_channel(x, W, w_scale, out_dtype=torch.bfloat16, out=None, workspace=None):
     """quant_act_token(x) then the channel-wise GEMM, in one call; x [M, K] bf16/fp16."""
     return _linear(lib.linear_w8a8_channel, W8_SCHEME_CHANNEL, x, W, w_scale, out_dtype, out, workspace)
+
+
+# ------------------------------------------------- asymmetric (per tensor)
+def quant_act_asym(x, out=None):
+    """Per-tensor asymmetric quantisation of x [M, K] (bf16 or fp16).
+
+    Returns (codes, params): int8 codes holding q - 128 for the uint8 code q,
+    and a device fp32 tensor [2] = (scale, zero point).
+    """
+    _dev(x)
+    M, K = x.shape
+    q, prm = out if out is not None else (_empty((M, K), torch.int8, x), _empty((2,), torch.float32, x))
+    _check(lib.quant_act_asym(_p(x), _act_dtype(x), M, K, _p(q), _p(prm), _stream()), "quant_act_asym")
+    return q, prm
+
+
+def weight_row_sums(W):
+    """int32 [N]: the sum of each row of the int8 weights W [N, K]."""
+    _dev(W)
+    N, K = W.shape
+    ws = _empty((N,), torch.int32, W)
+    _check(lib.weight_row_sums(_p(W), N, K, _p(ws), _stream()), "weight_row_sums")
+    return ws
+
+
+def gemm_w8a8_asym(A, a_params, W, w_scale, w_sum, out_dtype=torch.bfloat16, out=None):
+    """Asymmetric activations (quant_act_asym) times per-channel int8 weights."""
+    _dev(A, a_params, W, w_scale, w_sum)
+    M, K = A.shape
+    N = W.shape[0]
+    y = out if out is not None else _empty((M, N), out_dtype, A)
+    _check(lib.gemm_w8a8_asym(_p(A), _p(a_params), _p(W), _p(w_scale), _p(w_sum), _p(y), _out_code(y.dtype),
+                              M, N, K, _stream()), "gemm_w8a8_asym")
+    return y

@@ -32,7 +32,7 @@ LIB = os.path.join(HERE, "libw8a8.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["quant.hip", "gemm_tile.hip", "gemm_block.hip", "gemm_decode.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "gemm_tile.hip", "gemm_block.hip", "gemm_decode.hip", "asym.hip", "capi.cpp"]
 EXTRA_FLAGS = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC",

@@ -235,4 +235,40 @@ int linear_w8a8_channel(const void* x, int x_dtype, const int8_t* W, const float
   return linear_common(false, x, x_dtype, W, w_scale, Y, y_dtype, M, N, K, workspace, workspace_bytes, stream);
 }
 
+int quant_act_asym(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q_shifted, float* params,
+                   void* stream) {
+  if (x_dtype != W8_BF16 && x_dtype != W8_FP16) return W8_ERR_DTYPE;
+  int rc = check_rows_k(M, K);
+  if (rc) return rc;
+  if (M == 0 || K == 0) return W8_OK;
+  if (!x || !q_shifted || !params) return W8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q_shifted, 16) || !aligned(params, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_quant_asym(x, x_dtype == W8_FP16, M, K, q_shifted, params, as_stream(stream)));
+}
+
+int weight_row_sums(const int8_t* W, int64_t N, int64_t K, int32_t* w_sum, void* stream) {
+  int rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (K > (int64_t(1) << 16)) return W8_ERR_SHAPE;
+  if (N == 0) return W8_OK;
+  if (K == 0) return W8_ERR_SHAPE;
+  if (!W || !w_sum) return W8_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(w_sum, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_weight_row_sums(W, N, K, w_sum, as_stream(stream)));
+}
+
+int gemm_w8a8_asym(const int8_t* A_shifted, const float* a_params, const int8_t* W, const float* w_scale,
+                   const int32_t* w_sum, void* Y, int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  w8::OutKind out;
+  int rc = check_out(y_dtype, false, &out);
+  if (rc) return rc;
+  rc = check_gemm_common(A_shifted, W, Y, M, N, K);
+  if (rc || M == 0 || N == 0) return rc;
+  if (K == 0 || K > (int64_t(1) << 16)) return W8_ERR_SHAPE;
+  if (!a_params || !w_scale || !w_sum) return W8_ERR_NULL;
+  if (!aligned(a_params, 4) || !aligned(w_scale, 4) || !aligned(w_sum, 4)) return W8_ERR_ALIGN;
+  return status_of(
+      w8::launch_gemm_asym(A_shifted, a_params, W, w_scale, w_sum, Y, out, M, N, K, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -41,6 +41,28 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)h;
 }
 
+// 8 values from a 16-byte chunk of bf16 or fp16.
+template <bool FP16>
+__device__ __forceinline__ void unpack8(const uint4& c, float* v) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (FP16) {
+      v[2 * i] = h2f(w[i] & 0xffffu);
+      v[2 * i + 1] = h2f(w[i] >> 16);
+    } else {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+}
+
+__device__ __forceinline__ float amax_n(const float* v, int n) {
+  float a = 0.f;
+  for (int i = 0; i < n; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+  return a;
+}
+
 // ---------------------------------------------------------------- quantiser
 struct QScale {
   float s;   // the group scale, fp32(max(amax, eps) / 127)

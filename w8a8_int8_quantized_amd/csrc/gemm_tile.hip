@@ -32,10 +32,16 @@ namespace {
 // leave a quarter of the second round idle, 512 tiles of width 224 do not).
 constexpr int kChBM = 256;
 
-template <int OUT, int FN>
+// AS: the epilogue of the asymmetric per-tensor activations (codes stored as
+// q - 128, prm = {s, z}, wsum = per-row weight sums) in place of the
+// channel-wise one: Y = fp32(fp32(s * sw[n]) * fp32(fp32(ACC + 128 WS[n]) -
+// fp32(z * fp32(WS[n])))).
+template <int OUT, int FN, bool AS = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                         void* __restrict__ Y, int M, int N, int K, int TM) {
+                                                         void* __restrict__ Y, int M, int N, int K, int TM,
+                                                         const float* __restrict__ prm = nullptr,
+                                                         const int32_t* __restrict__ wsum = nullptr) {
   constexpr int kChBN = 32 * FN;
   constexpr int kChStage = (kChBM + kChBN) * 128;
   // two stages, or the bf16 epilogue's 256 rows of 512 bytes
@@ -141,19 +147,37 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
     return;
   }
   // this lane's 8 activation scales and 8 x 4 weight scales, all loads in
-  // flight at once
-  float sam[8], swn[FN][4];
+  // flight at once (asymmetric: per column fp32(s * sw), fp32(z * WS) and
+  // 128 WS instead)
+  float sam[8], swn[FN][4], zw[FN][4];
+  int wsx[FN][4];
+  if (!AS) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = m0 + wm * 128 + j * 16 + (lane & 15);
-    sam[j] = m < M ? sa[m] : 0.f;
+    for (int j = 0; j < 8; ++j) {
+      const int m = m0 + wm * 128 + j * 16 + (lane & 15);
+      sam[j] = m < M ? sa[m] : 0.f;
+    }
   }
+  const float as_s = AS ? prm[0] : 0.f, as_z = AS ? prm[1] : 0.f;
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
     const int n = n0 + wn * 16 * FN + i * 16 + 4 * (lane >> 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) swn[i][r] = n + r < N ? sw[n + r] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      swn[i][r] = n + r < N ? sw[n + r] : 0.f;
+      if (AS) {
+        const int ws = n + r < N ? wsum[n + r] : 0;
+        swn[i][r] = __fmul_rn(as_s, swn[i][r]);
+        zw[i][r] = __fmul_rn(as_z, (float)ws);
+        wsx[i][r] = 128 * ws;
+      }
+    }
   }
+  // output value of accumulator r of fragment (i, j)
+  auto outv = [&](int i, int j, int r) -> float {
+    if (AS) return __fmul_rn(swn[i][r], __fsub_rn((float)(acc[i][j][r] + wsx[i][r]), zw[i][r]));
+    return __fmul_rn((float)acc[i][j][r], __fmul_rn(sam[j], swn[i][r]));
+  };
   if (OUT == OUT_F32) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -165,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
         if (n >= N) continue;
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = __fmul_rn((float)acc[i][j][r], __fmul_rn(sam[j], swn[i][r]));
+        for (int r = 0; r < 4; ++r) o[r] = outv(i, j, r);
         store4<OUT_F32>(Y, (int64_t)m * N + n, n, N, vec, o[0], o[1], o[2], o[3]);
       }
     }
@@ -184,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
     for (int i = 0; i < FN; ++i) {
       uint32_t h[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(__fmul_rn((float)acc[i][j][q], __fmul_rn(sam[j], swn[i][q])));
+      for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(outv(i, j, q));
       const int chunk = wn * 2 * FN + 2 * i + (lane >> 5);
       *reinterpret_cast<uint2*>(smem + r * 512 + ((chunk ^ (r & 15)) << 4) + 8 * ((lane >> 4) & 1)) =
           make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
@@ -290,14 +314,32 @@ hipError_t channel_launch(const int8_t* A, const float* sa, const int8_t* W, con
   return hipGetLastError();
 }
 
+template <int FN>
+hipError_t channel_asym_launch(const int8_t* A, const float* prm, const int8_t* W, const float* sw,
+                               const int32_t* wsum, void* Y, OutKind out, int64_t M, int64_t N, int64_t K, int TM,
+                               hipStream_t st) {
+  const int TN = (int)((N + 32 * FN - 1) / (32 * FN));
+  const dim3 grid((unsigned)(TM * TN)), block(256);
+  if (out == OUT_F32)
+    hipLaunchKernelGGL((k_gemm_channel<OUT_F32, FN, true>), grid, block, 0, st, A, nullptr, W, sw, Y, (int)M,
+                       (int)N, (int)K, TM, prm, wsum);
+  else
+    hipLaunchKernelGGL((k_gemm_channel<OUT_BF16, FN, true>), grid, block, 0, st, A, nullptr, W, sw, Y, (int)M,
+                       (int)N, (int)K, TM, prm, wsum);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// Per-(device, stream) workspace for split-K partial tiles, grown on demand
-// and kept until the process ends.  Calls on one stream are ordered, so they
-// may share it; different streams get different buffers.
+// Per-(device, stream, slot) workspaces, grown on demand and kept until the
+// process ends: slot 0 holds split-K partial tiles, slot 1 the asymmetric
+// GEMM's int32 accumulators and its quantiser's partial ranges (a GEMM there
+// may split K into slot 0 at the same time).  Calls on one stream are
+// ordered, so they may share a slot; different streams get different buffers.
 struct Workspace {
   int dev;
   hipStream_t st;
+  int slot;
   void* p;
   size_t bytes;
 };
@@ -326,13 +368,15 @@ int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_u
   return best;
 }
 
-hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) {
+hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) { return stream_workspace(st, 0, bytes, out); }
+
+hipError_t stream_workspace(hipStream_t st, int slot, size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lk(g_ws_mu);
   for (Workspace& w : g_ws) {
-    if (w.dev == dev && w.st == st) {
+    if (w.dev == dev && w.st == st && w.slot == slot) {
       if (w.bytes < bytes) {
         // the stream's earlier kernels may still read the old buffer
         e = hipStreamSynchronize(st);
@@ -352,9 +396,26 @@ hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) {
   void* p = nullptr;
   e = hipMalloc(&p, bytes);
   if (e != hipSuccess) return e;
-  g_ws.push_back({dev, st, p, bytes});
+  g_ws.push_back({dev, st, slot, p, bytes});
   *out = p;
   return hipSuccess;
+}
+
+bool channel_tiles_unsplit(int64_t M, int64_t N, int64_t K) {
+  if (decode_path_takes(M, N, true)) return false;
+  const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + 255) / 256);
+  return pick_k_slices((int64_t)TM * TN, K >> 7, M, N, 2.2) == 1;
+}
+
+hipError_t launch_gemm_channel_asym_tiles(const int8_t* A, const float* prm, const int8_t* W, const float* sw,
+                                          const int32_t* wsum, void* Y, OutKind out, int64_t M, int64_t N,
+                                          int64_t K, hipStream_t st) {
+  const int TM = (int)((M + kChBM - 1) / kChBM);
+  switch (pick_channel_width(TM, N)) {
+    case 7: return channel_asym_launch<7>(A, prm, W, sw, wsum, Y, out, M, N, K, TM, st);
+    case 6: return channel_asym_launch<6>(A, prm, W, sw, wsum, Y, out, M, N, K, TM, st);
+    default: return channel_asym_launch<8>(A, prm, W, sw, wsum, Y, out, M, N, K, TM, st);
+  }
 }
 
 hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,

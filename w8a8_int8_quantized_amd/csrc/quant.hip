@@ -18,22 +18,6 @@ namespace w8 {
 namespace {
 
 // ------------------------------------------------------------------ decode
-// 8 values from a 16-byte chunk of bf16 or fp16.
-template <bool FP16>
-__device__ __forceinline__ void unpack8(const uint4& c, float* v) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (FP16) {
-      v[2 * i] = h2f(w[i] & 0xffffu);
-      v[2 * i + 1] = h2f(w[i] >> 16);
-    } else {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
-    }
-  }
-}
-
 // OCP FP8-E4M3FN byte J of w -> fp32 (exact: gfx950's v_cvt_f32_fp8 decodes
 // the OCP encoding, bias 7, subnormals included; the GPU tests cover every
 // finite code), times scale_inv in fp32, rounded to bf16 (nearest even);
@@ -55,12 +39,6 @@ __device__ __forceinline__ void unpack16_fp8(const uint4& c, float scale_inv, fl
     v[4 * i + 2] = fp8_to_bf16_value<2>(w[i], scale_inv);
     v[4 * i + 3] = fp8_to_bf16_value<3>(w[i], scale_inv);
   }
-}
-
-__device__ __forceinline__ float amax_n(const float* v, int n) {
-  float a = 0.f;
-  for (int i = 0; i < n; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
-  return a;
 }
 
 // ------------------------------------------------------- per token-group
