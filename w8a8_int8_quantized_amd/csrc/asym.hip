@@ -23,7 +23,8 @@
 // The quantiser takes two launches: every workgroup of the first reduces its
 // share of the tensor to a partial (min, max); every workgroup of the second
 // reduces all partials (exact, so each derives the same s and z) and then
-// quantises its share.
+// quantises its share.  The quotient goes through a reciprocal estimate with
+// a tie check (proof at kAsymTieGuard), exact division deciding near ties.
 #include "common.h"
 #include "launch.h"
 
@@ -32,6 +33,13 @@ namespace {
 
 constexpr int kAsymMaxWgs = 1024;       // partial ranges per tensor
 constexpr float kURange = 255.0f;
+// Quotient estimate y = fp32(d * fp32(1 / s)) for 0 <= d / s <= 255.00003:
+// |y - d / s| <= (d / s)(2^-23 + 2^-48) < 3.05e-5, and the correctly rounded
+// fp32(d / s) lies within half an ulp (7.7e-6 below 256) of d / s, so the
+// two differ by less than 3.9e-5 < 2^-14.  If y is farther than 2^-14 from
+// every half-integer, both round to the same integer; otherwise the exact
+// division decides.
+constexpr float kAsymTieGuard = 0.49993896484375f;   // 0.5 - 2^-14
 
 // Block-wide min and max for a 256-thread workgroup, every thread gets both.
 __device__ __forceinline__ void block_minmax256(float& mn, float& mx, float* red4) {
@@ -75,6 +83,7 @@ __global__ __launch_bounds__(256) void k_quant_asym(const uint4* __restrict__ x,
   block_minmax256(mn, mx, red);
   const float s = fmaxf(__fsub_rn(mx, mn), kEps) / kURange;   // correctly rounded fp32 divisions
   const float z = -mn / s;
+  const float r = 1.0f / s;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     params[0] = s;
     params[1] = z;
@@ -85,7 +94,11 @@ __global__ __launch_bounds__(256) void k_quant_asym(const uint4* __restrict__ x,
     uint32_t b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float t = fminf(fmaxf(__builtin_rintf(__fsub_rn(v[i], mn) / s), 0.f), kURange);
+      const float d = __fsub_rn(v[i], mn);
+      const float y = __fmul_rn(d, r);
+      float t = __builtin_rintf(y);
+      if (__builtin_expect(__builtin_fabsf(__fsub_rn(y, t)) > kAsymTieGuard, 0)) t = __builtin_rintf(d / s);
+      t = fminf(fmaxf(t, 0.f), kURange);
       b[i] = (uint32_t)((int)t - 128) & 0xffu;
     }
     q[c] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
