@@ -340,7 +340,45 @@ def cpu_baseline():
     return {"value": round(ops / t / 1e12, 4), "unit": "TOPS", "cores": int(cores), "kind": "oracle",
             "sample": f"the full channel-wise MLP step ({Ms} tokens, gate_up N={Ngs}, down N={Nds}); "
                       f"median of 5 runs of {t:.2f} s",
-            "seconds": round(t, 3)}
+            "seconds": round(t, 3), "cpu_model": _cpu_model(), "tiny": _oracle_tiny()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:                                             # pragma: no cover
+        pass
+    return "unknown"
+
+
+def _oracle_tiny():
+    """The oracle on the tiny block-wise case (16 tokens, K = 256 -> N = 256:
+    group quantisation, tile quantisation of the weights, block-wise GEMM),
+    median of 5 wall-clock runs in ms, with all BLAS threads and with one."""
+    import numpy as np
+    import synth
+    from oracle import gemm as ogemm, quant as oquant
+    x = synth.to_numpy(synth.activations(16, 256, seed=0, outlier_frac=0.01, outlier_factor=20.0))
+    w = synth.to_numpy(synth.weights(256, 256, seed=1))
+
+    def once():
+        t0 = time.perf_counter()
+        qa, sa = oquant.quant_act_group(x)
+        qw, sw = oquant.quant_weight_block(w)
+        ogemm.gemm_block(qa, sa, qw, sw)
+        return (time.perf_counter() - t0) * 1e3
+
+    out = {"workload": "M=16, K=256, N=256 block-wise (quantisers + GEMM)",
+           "ms_all_threads": round(float(np.median([once() for _ in range(5)])), 3)}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            out["ms_1_thread"] = round(float(np.median([once() for _ in range(5)])), 3)
+    except Exception:                                           # pragma: no cover
+        out["ms_1_thread"] = None
+    return out
 
 
 def main():
