@@ -4,8 +4,9 @@ The DeepSeek-V3 dense MLP at 4096 tokens: gate_up (K = 7168 -> N = 36864)
 and down (K = 18432 -> N = 7168), channel-wise (the headline step) and
 block-wise (bf16 weights quantised per 128 x 128 block by the oracle; the
 benchmark's block rows reach INT8 codes of the same shapes through the FP8
-requantisation, whose plain oracle decode is too slow at this size for a
-GPU test).  The GPU runs the whole GEMM through
+requantisation, checked below on sampled 128 x 128 tiles of the full-size
+conversion: every tile depends only on its own codes and scale_inv).  The
+GPU runs the whole GEMM through
 the same entry points and output types as the benchmark, so the same kernels
 and launch configuration; the oracle recomputes a sample: every output
 depends only on its row of A (with that row's scales) and its row of W (with
@@ -97,6 +98,27 @@ def test_block_full_size_sampled(name):
     gotb = _pick(yb.view(torch.int16), rows, cols).view(np.uint16)
     assert np.array_equal(gotb, formats.f32_to_bf16_bits(got32))
     assert gemm.normwise_rel_err(formats.bf16_bits_to_f32(gotb).astype(np.float64), y64) <= 1e-2
+
+
+# FP8 -> BF16 -> INT8 conversion of the whole gate_up weight (36864 x 7168,
+# the benchmark's requantisation row, inputs drawn on the GPU as the
+# benchmark draws them); the oracle converts four sampled tiles (the first,
+# the last and two at random) from the same codes and scale_inv.
+def test_requant_fp8_full_size_sampled():
+    K, N = SHAPES["gate_up"]
+    NB, KB = N // 128, K // 128
+    print(f"requant fp8: N={N} K={K}", flush=True)
+    codes, si = synth.fp8_weights(N, K, seed=synth.SEEDS["block"], device=DEV)
+    q, sc, wb = w8.requant_fp8_to_int8_block(codes, si, return_bf16=True)
+    rng = np.random.default_rng(91)
+    tiles = sorted({(0, 0), (NB - 1, KB - 1), (int(rng.integers(NB)), int(rng.integers(KB))),
+                    (int(rng.integers(NB)), int(rng.integers(KB)))})
+    for nb, kb in tiles:
+        r, c = slice(nb * 128, (nb + 1) * 128), slice(kb * 128, (kb + 1) * 128)
+        oq, osc, owb = quant.requant_fp8_to_int8_block(_np(codes[r, c]), _np(si[nb:nb + 1, kb:kb + 1]))
+        assert np.array_equal(_np(q[r, c]), oq), (nb, kb)
+        assert _np(sc[nb:nb + 1, kb:kb + 1]).view(np.uint32)[0, 0] == osc.view(np.uint32)[0, 0], (nb, kb)
+        assert np.array_equal(_np(wb[r, c].contiguous().view(torch.int16)).view(np.uint16), owb), (nb, kb)
 
 
 # ------------------------------------------------------------ decode shapes
