@@ -310,7 +310,7 @@ def rows(args):
 def cpu_baseline():
     """The CPU oracle as it stands on the headline step itself (all 4096
     tokens, all output channels), median of 5 runs: about 15-20 s of CPU
-    work on the GPU machine's host threads."""
+    work on the host's threads."""
     import numpy as np
     import synth
     from oracle import gemm as ogemm, quant as oquant
@@ -384,7 +384,7 @@ def _oracle_tiny():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
