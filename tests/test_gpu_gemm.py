@@ -400,3 +400,39 @@ def test_empty_gemms_are_noops():
     W = torch.zeros(128, 256, dtype=torch.int8, device=DEV)
     SW = torch.ones(1, 2, dtype=torch.float32, device=DEV)
     assert w8.gemm_w8a8_block(A, SA, W, SW).shape == (0, 128)
+
+
+def test_split_workspaces_are_per_stream():
+    """Split-K GEMMs (partials in the library's per-stream workspace) and the
+    asymmetric decode GEMM (int32 accumulators in the second workspace) on
+    two streams at once give the same bits as on one stream."""
+    M, N, K = 512, 1536, 7168          # few tiles: the block and channel GEMMs split K
+    outs = {}
+    inputs = []
+    for i in range(2):
+        qa, sa = quant.quant_act_group(synth.to_numpy(synth.activations(M, K, seed=140 + i)))
+        qw, sw = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=150 + i)))
+        qt, st = quant.quant_act_token(synth.to_numpy(synth.activations(M, K, seed=160 + i)))
+        qc, sc = quant.quant_act_token(synth.to_numpy(synth.weights(N, K, seed=170 + i)))
+        inputs.append([torch.from_numpy(a).to(DEV) for a in (qa, sa, qw, sw, qt, st, qc, sc)])
+
+    def run(t):
+        A, SA, W, SW, AT, ST, WC, SC = t
+        yb = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+        yc = w8.gemm_w8a8_channel(AT, ST, WC, SC, out_dtype=torch.float32)
+        prm = torch.tensor([0.01, 3.5], device=DEV)
+        ya = w8.gemm_w8a8_asym(AT[:8].contiguous(), prm, WC, SC, w8.weight_row_sums(WC), out_dtype=torch.float32)
+        return yb, yc, ya
+
+    ref = [run(t) for t in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for i, s in enumerate(streams):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                outs[i] = run(inputs[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            for got, want in zip(outs[i], ref[i]):
+                assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (rep, i)
