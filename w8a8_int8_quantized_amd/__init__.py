@@ -12,6 +12,8 @@ fallback: if libw8a8.so is missing, importing this package raises.
     y = gemm_w8a8_block(q, s, wq, ws)          # bf16 (or fp32) output
     y = gemm_w8a8_channel(q, s, wq, ws)
     y = linear_w8a8_block(x, wq, ws)           # quant_act_group + gemm_w8a8_block in one call
+    qa, prm = quant_act_asym(x)                # asymmetric per-tensor uint8 (stored as q - 128)
+    y = gemm_w8a8_asym(qa, prm, wq, ws, weight_row_sums(wq))   # per-channel weights
 """
 
 import ctypes
