@@ -119,3 +119,23 @@ def test_gemm_asym_full_size_sampled():
     _, _, y64, y32 = asym.gemm_asym(q[rows], s, z, qw[cols], sw[cols])
     got = _np(y.index_select(0, torch.from_numpy(rows).to(DEV)).index_select(1, torch.from_numpy(cols).to(DEV)))
     assert np.array_equal(got.view(np.uint32), y32.view(np.uint32))
+
+
+def test_gemm_asym_max_k_extreme_codes():
+    """K = 2^16, the limit: every code 255 but one 0 per row and every weight
+    code 127, so ACC = 255 * 127 * (K - 1) = 2.12e9 sits just inside int32
+    (and the stored codes' sum 127 * 127 * (K - 1) plus 128 WS as well)."""
+    M, N, K = 2, 3, 1 << 16
+    x = torch.ones(M, K, dtype=torch.bfloat16)
+    x[:, 0] = -1.0
+    q, s, z = asym.quant_act_asym(synth.to_numpy(x))
+    assert q[:, 1:].min() == 255 and q[:, 0].max() == 0
+    qw, sw = quant.quant_act_token(synth.to_numpy(torch.full((N, K), 0.02, dtype=torch.bfloat16)))
+    assert (qw == 127).all()
+    ACC, _, y64, y32 = asym.gemm_asym(q, s, z, qw, sw)
+    assert ACC.max() == 255 * 127 * (K - 1) < 2 ** 31
+    codes, prm = w8.quant_act_asym(x.to(DEV))
+    assert np.array_equal(_np(codes).view(np.uint8) ^ 0x80, q)
+    W, SW = (torch.from_numpy(a).to(DEV) for a in (qw, sw))
+    got = _np(w8.gemm_w8a8_asym(codes, prm, W, SW, w8.weight_row_sums(W), out_dtype=torch.float32))
+    assert np.array_equal(got.view(np.uint32), y32.view(np.uint32))

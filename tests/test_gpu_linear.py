@@ -76,7 +76,7 @@ def test_linear_block(M, N, K, fp16):
 
 
 @pytest.mark.parametrize("fp16", [False, True])
-@pytest.mark.parametrize("M,N,K", CASES)
+@pytest.mark.parametrize("M,N,K", CASES + WIDE)
 def test_linear_channel(M, N, K, fp16):
     print(f"linear channel M={M} N={N} K={K} fp16={fp16}", flush=True)
     x, xo, w = _inputs(M, N, K, seed=M + 21, fp16=fp16)
