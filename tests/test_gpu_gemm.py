@@ -436,3 +436,42 @@ def test_split_workspaces_are_per_stream():
         for i in range(2):
             for got, want in zip(outs[i], ref[i]):
                 assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (rep, i)
+
+
+def test_graph_capture_replays_match_eager():
+    """The GEMM paths launch no memsets and allocate nothing once a stream's
+    workspace has grown, so a captured HIP graph (split-K block-wise GEMM,
+    one-call linear layer, split-K channel-wise GEMM) replays to the eager
+    bits; eager overwrites and synchronisations run between the replays."""
+    M, N, K = 512, 1536, 7168
+    qa, sa = quant.quant_act_group(synth.to_numpy(synth.activations(M, K, seed=180)))
+    qw, sw = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=181)))
+    qt, st = quant.quant_act_token(synth.to_numpy(synth.activations(M, K, seed=182)))
+    qc, sc = quant.quant_act_token(synth.to_numpy(synth.weights(N, K, seed=183)))
+    A, SA, W, SW, AT, ST, WC, SC = (torch.from_numpy(a).to(DEV) for a in (qa, sa, qw, sw, qt, st, qc, sc))
+    x = synth.activations(8, 4096, seed=184).to(DEV)
+    qd, sd = quant.quant_weight_block(synth.to_numpy(synth.weights(12288, 4096, seed=185)))
+    WD, SWD = torch.from_numpy(qd).to(DEV), torch.from_numpy(sd).to(DEV)
+    ws = torch.empty(w8.linear_workspace_bytes(w8.W8_SCHEME_BLOCK, 8, 4096), dtype=torch.uint8, device=DEV)
+
+    def step():
+        return (w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32),
+                w8.linear_w8a8_block(x, WD, SWD, out_dtype=torch.float32, workspace=ws),
+                w8.gemm_w8a8_channel(AT, ST, WC, SC, out_dtype=torch.float32))
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ref = [t.clone() for t in step()]          # grows this stream's workspaces
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        outs = step()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o.view(torch.int32), r.view(torch.int32)), rep
