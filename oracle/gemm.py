@@ -93,22 +93,26 @@ def gemm_w8a16_group(x, Wq, w_scale):
         Y[m, n] = sum_g w_scale[n, g] * sum_{k in g} x[m, k] * Wq[n, k]
 
     x: fp16 [M, K]; Wq int8 [N, K]; w_scale fp32 [N, K/128].
-    Returns (y64, y32) where y32 takes each group's dot product in fp32 and
-    accumulates acc = fp32(acc + fp32(s * partial)) over groups in order.
+    Returns (y64, y32).  y32 is evaluated in fp32 in a fixed order: inside
+    each group the dot product runs k = 128 g, 128 g + 1, ... with
+    partial = fp32(partial + fp32(x * q)) (every product of an fp16 value and
+    an int8 code is exact in fp32, so only the sums round), then across
+    groups acc = fp32(acc + fp32(s * partial)) for g = 0, 1, ...
     """
     x32 = widen(x)
     M, K = x32.shape
     N = Wq.shape[0]
     KB = K // GROUP
     s = np.asarray(w_scale, F32).reshape(N, KB)
+    wq32 = np.asarray(Wq).astype(F32)
     y64 = np.zeros((M, N), F64)
     acc = np.zeros((M, N), F32)
     for g in range(KB):
         ks = slice(g * GROUP, (g + 1) * GROUP)
-        xa = x32[:, ks]
-        wq = Wq[:, ks]
-        y64 += (xa.astype(F64) @ wq.astype(F64).T) * s[:, g].astype(F64)[None, :]
-        part = (xa @ wq.astype(F32).T).astype(F32)
+        y64 += (x32[:, ks].astype(F64) @ wq32[:, ks].astype(F64).T) * s[:, g].astype(F64)[None, :]
+        part = np.zeros((M, N), F32)
+        for k in range(g * GROUP, (g + 1) * GROUP):
+            part = (part + x32[:, k][:, None] * wq32[:, k][None, :]).astype(F32)
         acc = (acc + (s[:, g][None, :] * part).astype(F32)).astype(F32)
     return y64, acc
 

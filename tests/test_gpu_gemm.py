@@ -254,10 +254,10 @@ def test_w8a16_rows_independent_of_next_row(M, N, K):
     assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
 
 
-# K split over workgroups with the slices reduced by the last workgroup of
-# each column tile: N not a multiple of 4 (scalar reduction), and repeated
-# calls on one stream (each call's counters must be left at zero for the next,
-# or a later call writes no output for some tiles).
+# K split over workgroups, each slice writing fp32 partials that a second
+# kernel (k_w16_slices_sum) sums in slice order: N not a multiple of 4 (the
+# reduction's scalar tail), and repeated calls on one stream sharing the
+# stream's workspace.
 def _w8a16_case(M, N, K, seed):
     x = synth.activations(M, K, seed=seed, dtype=torch.float16)
     w = synth.weights(N, K, seed=seed + 1, dtype=torch.float16)

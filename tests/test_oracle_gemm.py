@@ -211,3 +211,64 @@ def test_grouped_gemm_rowwise_against_dequantised_expert_weights():
     # quantise-then-gather equals gather-then-quantise (the quantiser is row-local)
     Aq_all, sa_all = quant.quant_act_group(x)
     assert np.array_equal(Aq_all[rows], Aq) and np.array_equal(sa_all[rows], sa)
+
+
+def test_w8a16_y32_within_fixed_order_fp32_bound():
+    """y32 is a fixed-order fp32 evaluation: 128 sequential sums inside each
+    group and KB sequential sums across groups.  Against the exact rational
+    value each output lies within (128 + KB + 2) 2^-24 of the sum of the
+    absolute terms (a dropped group, a wrong scale index or fp16 rounding of
+    the partials would break it)."""
+    M, K, N = 2, 384, 3
+    x = synth.activations(M, K, seed=31, dtype=__import__("torch").float16).numpy()
+    w = synth.weights(N, K, seed=32, dtype=__import__("torch").float16).numpy()
+    Wq, s = quant.quant_act_group(w)
+    _, y32 = gemm.gemm_w8a16_group(x, Wq, s)
+    KB = K // 128
+    for m in range(M):
+        for n in range(N):
+            exact, mag = Fraction(0), Fraction(0)
+            for g in range(KB):
+                terms = [Fraction(float(x[m, k])) * int(Wq[n, k]) for k in range(g * 128, g * 128 + 128)]
+                exact += Fraction(float(s[n, g])) * sum(terms)
+                mag += abs(Fraction(float(s[n, g]))) * sum(abs(t) for t in terms)
+            assert abs(Fraction(float(y32[m, n])) - exact) <= (128 + KB + 2) * Fraction(1, 2 ** 24) * mag
+
+
+def test_w8a16_y32_group_partials_are_not_rounded_to_fp16():
+    """A group whose fp32 partial is not representable in fp16 (2049 = 2^11 + 1
+    is exact in fp32 but not in fp16) keeps its value: with unit scale and
+    x = 1 everywhere, Y = sum of the codes exactly."""
+    K = 256
+    x = np.ones((1, K), np.float16)
+    Wq = np.zeros((1, K), np.int8)
+    Wq[0, :17] = 121            # 17 * 121 = 2057 in group 0 (odd, > 2048)
+    Wq[0, 128:130] = (-1, 3)    # 2 in group 1
+    s = np.ones((1, 2), np.float32)
+    y64, y32 = gemm.gemm_w8a16_group(x, Wq, s)
+    assert y64[0, 0] == 2059.0 and y32[0, 0] == np.float32(2059.0)
+
+
+def test_normwise_rel_err_hand_worked():
+    """The comparison of every float parity check: max|y - ref| / max|ref| over
+    the whole tensor (reading R12), worked by hand."""
+    ne = gemm.normwise_rel_err
+    # denominator is max|ref| = 4, not max|y| = 3, and not a mean
+    assert ne(np.array([1.0, 2.0, 3.0]), np.array([1.0, 2.0, 4.0])) == 0.25
+    # a negative entry dominates: max|ref| = 8 (max(ref) = 1 would give 2)
+    assert ne(np.array([-8.0, 3.0]), np.array([-8.0, 1.0])) == 0.25
+    # one outlier error on a small entry is measured against the largest
+    # entry (elementwise relative error would be 1.0 here)
+    assert ne(np.array([100.0, 1.0, 1.0, 2.0]), np.array([100.0, 1.0, 1.0, 1.0])) == 0.01
+    # the worst element decides (a mean of the errors would give 0.0125)
+    assert ne(np.array([10.0, 10.0, 10.0, 10.5]), np.array([10.0, 10.0, 10.0, 10.0])) == 0.05
+    # over the whole 2-D tensor, not per row: the row max is 2, the tensor max 4
+    y = np.array([[2.0, 0.0], [4.0, 1.0]])
+    r = np.array([[1.0, 0.0], [4.0, 1.0]])
+    assert ne(y, r) == 0.25
+    # zero reference: the absolute error; empty tensors compare equal
+    assert ne(np.array([0.0, -3.0, 1.0]), np.zeros(3)) == 3.0
+    assert ne(np.zeros(0), np.zeros(0)) == 0.0
+    # symmetric in the sign of the difference, exact on equal inputs
+    assert ne(np.array([1.0, -5.0]), np.array([1.0, -4.0])) == ne(np.array([1.0, -3.0]), np.array([1.0, -4.0]))
+    assert ne(r, r) == 0.0

@@ -186,3 +186,76 @@ def test_fp16_and_bf16_inputs_give_the_same_codes_for_common_values(dtype):
     q, s = quant.quant_act_group(x)
     q2, s2 = quant.quant_act_group(v)
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_requant_channel_hand_worked():
+    """FP8 -> BF16 -> per-output-channel INT8 (page 1 section 2.3, channel-wise
+    paragraph), worked by hand on two 128-row tile rows and two K blocks with a
+    different scale_inv per tile, so that each row's amax spans both K blocks:
+
+      rows 0..127:  codes 0x30 (0.5) x 5    = 2.5   in K block 0,
+                    codes 0x38 (1.0) x 127  = 127   in K block 1
+                    -> amax 127, s = 1 exactly, q = rne(2.5) = 2 and 127;
+      rows 128,129: codes 0x38 (1.0) x 15.875 = 15.875 in K block 0,
+                    codes 0x34 (0.75) x 0.25 = 0.1875 and 0xB4 -> -0.1875
+                    in K block 1
+                    -> amax 15.875, s = 0.125 exactly, q = 127 and
+                    rne(+-1.5) = +-2.
+
+    Every product above is exact in fp32 and bf16.  Indexing scale_inv by the K
+    block alone, taking a 128 x 128 tile's amax instead of the row's, or
+    rounding half away from zero each changes some code or scale."""
+    N, K = 130, 256
+    codes = np.zeros((N, K), np.uint8)
+    codes[:128, :128] = 0x30
+    codes[:128, 128:] = 0x38
+    codes[128:, :128] = 0x38
+    codes[128:, 128:] = 0x34
+    codes[129, 128:] = 0xB4
+    si = np.array([[5.0, 127.0], [15.875, 0.25]], np.float32)
+    q, s, wb = quant.requant_fp8_to_int8_channel(codes, si)
+    assert s.shape == (N,)
+    assert np.all(s[:128] == np.float32(1.0)) and np.all(s[128:] == np.float32(0.125))
+    assert np.all(q[:128, :128] == 2) and np.all(q[:128, 128:] == 127)
+    assert np.all(q[128:, :128] == 127)
+    assert np.all(q[128, 128:] == 2) and np.all(q[129, 128:] == -2)
+    w = formats.bf16_bits_to_f32(wb)
+    assert np.all(w[:128, :128] == 2.5) and np.all(w[129, 128:] == np.float32(-0.1875))
+
+
+def test_requant_channel_matches_library_cast_route_and_rational_scales():
+    """torch's own casts give the bf16 weights (fp8 -> fp32, times the tile's
+    scale_inv, -> bf16); each row's scale is the correctly rounded
+    fp32(amax / 127) of the row's largest magnitude (checked with fractions),
+    and sampled codes are rne of the correctly rounded quotient."""
+    N, K = 200, 384
+    codes, si = synth.fp8_weights(N, K, seed=14)
+    f = codes.view(torch.float8_e4m3fn).to(torch.float32)
+    rows = torch.arange(N) // 128
+    cols = torch.arange(K) // 128
+    wb = (f * si[rows][:, cols]).to(torch.bfloat16)
+    q, s, wbits = quant.requant_fp8_to_int8_channel(codes.numpy(), si.numpy())
+    assert np.array_equal(wbits, synth.to_numpy(wb))
+    w = wb.to(torch.float32).numpy()
+    rng = np.random.default_rng(3)
+    for n in list(rng.choice(N, 12, replace=False)) + [0, 127, 128, N - 1]:
+        amax = Fraction(float(np.abs(w[n]).max()))
+        assert s[n] == _round_to_f32(amax / 127), n
+        for k in rng.choice(K, 16, replace=False):
+            quo = _round_to_f32(Fraction(float(w[n, k])) / Fraction(float(s[n])))
+            assert q[n, k] == int(np.rint(quo)), (n, k)
+
+
+def test_requant_channel_power_of_two_equivariance_per_tile_row():
+    """scale_inv = 2^e[nb] constant along a tile row: every row n keeps its
+    codes and its scale is multiplied by 2^e[n // 128] exactly (a scale_inv
+    looked up by the K block, or by the wrong tile row, breaks it)."""
+    N, K = 300, 384
+    codes, _ = synth.fp8_weights(N, K, seed=15)
+    codes = codes.numpy()
+    q0, s0, _ = quant.requant_fp8_to_int8_channel(codes, np.ones((3, 3), np.float32))
+    exps = np.array([-6.0, 4.0, 11.0])
+    si = np.repeat((2.0 ** exps)[:, None], 3, axis=1).astype(np.float32)
+    q1, s1, _ = quant.requant_fp8_to_int8_channel(codes, si)
+    assert np.array_equal(q0, q1)
+    assert np.array_equal(s1, (s0 * (2.0 ** exps)[np.arange(N) // 128]).astype(np.float32))

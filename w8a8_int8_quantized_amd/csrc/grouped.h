@@ -4,8 +4,10 @@
 // (off[e] .. off[e + 1] - 1 belong to expert e; off is non-decreasing, with
 // off[0] = 0 and off[E] = P).  Each expert's rows are cut into BM-row tiles,
 // and tiles are numbered in expert order; group_tile maps a tile number to its
-// expert and row range.  Method reference: "DeepSeek R1 INT8 quantisation in
-// SGLang" (Meituan), MoE section (per-expert block-wise INT8 weights).
+// expert and row range.  Method reference: the block-wise scheme of "DeepSeek
+// R1 INT8 quantisation in SGLang" (Meituan), section 2.3, applied per expert;
+// that DeepSeek's feed-forward layers are mixture-of-experts is stated on
+// "FP8 vs INT8 quantisation for DeepSeek", section 1.2.
 #pragma once
 
 #include "common.h"
