@@ -371,8 +371,11 @@ def test_grouped_moe_gemm(E, T, topk, K, N, empty, hot):
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(y))
 
 
+# 65..128 rows on N that balances over the CUs: the workgroup-shared decode
+# kernel with eight 16-row fragments per wave; its int32, fp32 and bf16
+# epilogues.
 @pytest.mark.parametrize("N", [12280, 36856])
-@pytest.mark.parametrize("M", [80, 128])
+@pytest.mark.parametrize("M", [80, 100, 128])
 def test_channel_up_to_128_rows_wide(M, N):
     K = 640
     qa, sa, qw, sw = _inputs(M, N, K, seed=M + N + 7, scheme="channel")
@@ -381,6 +384,8 @@ def test_channel_up_to_128_rows_wide(M, N):
     assert np.array_equal(_np(w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)), ACC)
     yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
     assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
+    yb = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
 
 
 def test_gemms_are_deterministic():

@@ -21,40 +21,61 @@ namespace {
 
 // ------------------------------------------------------------ channel-wise
 // 256 (m) x BN (n) output tile per workgroup, BN = 32 FN (FN = 8, 7 or 6);
-// 4 waves in a 2 (n) x 2 (m) grid, each wave 16 FN x 128 (FN x 8 fragments
-// of v_mfma_i32_16x16x64_i8, up to 256 int32 accumulators per lane in
-// AGPRs).  An LDS slot holds one K block: A 256 x 128 B then W BN x 128 B.
-// The loop runs over 64-wide K steps; the fragments of step t+1 are read
-// from LDS while step t's MFMAs run, and every second step (a K block
-// boundary) waits for the next block's DMA, synchronises, and starts the DMA
-// of the block after it.  Narrower tiles let the launcher fill the last
-// round of workgroups (e.g. N = 7168 at M = 4096: 448 tiles of width 256
-// leave a quarter of the second round idle, 512 tiles of width 224 do not).
+// 8 waves, two per SIMD, in a 2 (n) x 4 (m) grid, each wave 16 FN (n) x 64
+// (m): FN x 4 fragments of v_mfma_i32_16x16x64_i8, FN x 16 int32
+// accumulators per lane.  With two waves per SIMD one issues MFMAs while the
+// other waits on LDS or issues loads, and the LDS serves about twice the read
+// bandwidth it gives one wave per SIMD.
+//
+// K runs in 128-deep blocks through two LDS stages (A 256 x 128 B, then W
+// BN x 128 B).  A block is two 64-deep K steps, and the loop body is
+// unrolled over them so that the fragment registers alternate between two
+// sets without copies.  Step A of block kb multiplies (kb, first half) and
+// reads (kb, second half); then every wave waits for its loads of block kb+1
+// and for its own reads, and all meet at a barrier; step B multiplies (kb,
+// second half), reads (kb+1, first half) and loads block kb+2 into the stage
+// block kb has just left.  A wave's eight loads of a block (1 KB each: eight
+// rows of 128 B) go two at a time before the first four of its FN groups of
+// four MFMAs in step B, so no burst of loads stalls a wave's MFMAs.  The last
+// block is peeled (a branch inside the loop body breaks the in-place
+// accumulator allocation), and loads of blocks past the end are pushed
+// outside the descriptors' ranges: they move no data.
+//
+// A load that finds nothing in range still writes zeros to LDS (measured on
+// gfx950), so a wave without an eighth W row block (BN < 256) sends that
+// load to a junk kilobyte past the two stages, never onto the other stage.
+//
+// Tile order: workgroup b runs on XCD b % 8, and XCD x owns a contiguous band
+// of the tile sequence; the sequence walks strips of GM row tiles (m fastest
+// within a strip), so the 32 CUs of an XCD work on about GM row tiles x 32/GM
+// column tiles at a time and share both operands' panels in their L2.
 constexpr int kChBM = 256;
+constexpr unsigned kChOob = 0x20000000u;   // added to a load's offset: past every range
 
 // AS: the epilogue of the asymmetric per-tensor activations (codes stored as
 // q - 128, prm = {s, z}, wsum = per-row weight sums) in place of the
 // channel-wise one: Y = fp32(fp32(s * sw[n]) * fp32(fp32(ACC + 128 WS[n]) -
 // fp32(z * fp32(WS[n])))).
 template <int OUT, int FN, bool AS = false>
-__global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restrict__ A, const float* __restrict__ sa,
+__global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                         void* __restrict__ Y, int M, int N, int K, int TM,
+                                                         void* __restrict__ Y, int M, int N, int K, int TM, int GM,
                                                          const float* __restrict__ prm = nullptr,
                                                          const int32_t* __restrict__ wsum = nullptr) {
-  constexpr int kChBN = 32 * FN;
-  constexpr int kChStage = (kChBM + kChBN) * 128;
-  // two stages, or the bf16 epilogue's 256 rows of 512 bytes
-  constexpr int kSmem = 2 * kChStage > kChBM * 512 ? 2 * kChStage : kChBM * 512;
+  constexpr int BN = 32 * FN;
+  constexpr int kStage = (kChBM + BN) * 128;
+  constexpr int kJunk = 2 * kStage;
+  // two stages and the junk kilobyte, or the bf16 epilogue's 256 rows of 512 B
+  constexpr int kSmem = kJunk + 1024 > kChBM * 512 ? kJunk + 1024 : kChBM * 512;
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   int tm, tn;
-  xcd_tile(blockIdx.x, TM, (int)gridDim.x / TM, tm, tn);
-  const int m0 = tm * kChBM, n0 = tn * kChBN;
+  strip_tile(blockIdx.x, TM, (int)gridDim.x / TM, GM, tm, tn);
+  const int m0 = tm * kChBM, n0 = tn * BN;
   const int mval = M - m0 < kChBM ? M - m0 : kChBM;
-  const int nval = N - n0 < kChBN ? N - n0 : kChBN;
+  const int nval = N - n0 < BN ? N - n0 : BN;
   // split-K: slice blockIdx.y of gridDim.y covers K blocks kbs .. kbe - 1 and
   // writes its raw int32 tile to slice blockIdx.y of Y (M x N each)
   const int KBt = K >> 7;
@@ -65,78 +86,121 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   // still fall outside their range
   const v4i ra = make_rsrc(A + (int64_t)m0 * K + kbs * 128, (uint32_t)(mval * K - kbs * 128));
   const v4i rw = make_rsrc(W + (int64_t)n0 * K + kbs * 128, (uint32_t)(nval * K - kbs * 128));
-  const int voff = wave * 64 * K + dma_lane_off(lane, K);        // wave fills A rows 64*wave .. +63
-  const int voffw = wave * 8 * FN * K + dma_lane_off(lane, K);   // and W rows 8*FN*wave .. +8*FN-1
-  const uint32_t lds0 = lds_addr(smem);
   const int NK = kbe - kbs;
+  const int voff = dma_lane_off(lane, K);
+  const uint32_t lds0 = lds_addr(smem);
   const int K8 = 8 * K;
-  const int lo0 = frag_off(lane & 15, lane >> 4);           // 16x16x64 operand: row l%16, chunk l/16
+  const int lo0 = frag_off(lane & 15, lane >> 4);            // 16x16x64 operand: row l % 16, chunk l / 16
   const int lo1 = frag_off(lane & 15, 4 + (lane >> 4));
+  // load d (0..7) of a block: A row block wave + 8 d (d < 4), W row block
+  // wave + 8 (d - 4); the eighth exists when wave + 24 < 4 FN
+  const bool w8th = wave + 24 < 4 * FN;
+  const int soff0 = wave * K8;
+  const uint32_t dlds0 = lds0 + wave * 1024;
+  const uint32_t ljunk = lds0 + kJunk;
 
-  v4i acc[FN][8];
+  v4i acc[FN][4];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
-#define CH_DMA(T)                                                                                  \
+#define CH_LOAD(T, D, SO)                                                                          \
   {                                                                                               \
-    const uint32_t base = lds0 + ((T) & 1) * kChStage;                                            \
-    _Pragma("unroll") for (int b = 0; b < 8; ++b)                                                 \
-      dma16(ra, voff, b * K8 + (T) * 128, base + wave * 8192 + b * 1024);                         \
-    _Pragma("unroll") for (int b = 0; b < FN; ++b)                                                \
-      dma16(rw, voffw, b * K8 + (T) * 128, base + kChBM * 128 + wave * FN * 1024 + b * 1024);     \
+    const uint32_t base = dlds0 + ((T) & 1) * kStage;                                             \
+    if ((D) < 4) {                                                                                \
+      dma16(ra, voff, soff0 + 8 * (D) * K8 + (T) * 128 + (SO), base + 8 * (D) * 1024);            \
+    } else if ((D) < 7) {                                                                         \
+      dma16(rw, voff, soff0 + 8 * ((D) - 4) * K8 + (T) * 128 + (SO), base + kChBM * 128 + 8 * ((D) - 4) * 1024); \
+    } else {                                                                                      \
+      dma16(rw, voff, soff0 + 24 * K8 + (T) * 128 + (SO) + (w8th ? 0u : kChOob),                  \
+            w8th ? base + kChBM * 128 + 24 * 1024 : ljunk);                                       \
+    }                                                                                             \
   }
-#define CH_RD(KS, WF, AF)                                                                          \
+#define CH_READ(BLK, LO, WF, AF, R)                                                                \
   {                                                                                               \
-    const char* buf = smem + (((KS) >> 1) & 1) * kChStage;                                        \
-    const int lo = ((KS) & 1) ? lo1 : lo0;                                                        \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) AF[j] = *(const v4i*)(buf + (wm * 128 + j * 16) * 128 + lo); \
-    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                                \
-      WF[i] = *(const v4i*)(buf + kChBM * 128 + (wn * 16 * FN + i * 16) * 128 + lo);              \
+    const char* buf = smem + ((BLK) & 1) * kStage;                                                \
+    if ((R) < 4) AF[(R)] = *(const v4i*)(buf + (wm * 64 + (R) * 16) * 128 + (LO));                \
+    else WF[(R) - 4] = *(const v4i*)(buf + kChBM * 128 + (wn * 16 * FN + ((R) - 4) * 16) * 128 + (LO)); \
+  }
+  // one K step: FN groups of four MFMAs (one W fragment against the four
+  // activation fragments); before group g, two of the 4 + FN reads of the
+  // next fragments (RD) and two of the eight loads of block LT (LD)
+#define CH_STEP(WC, AC, RD, RBLK, RLO, WN_, AN_, LD, LT, LSO)                                       \
+  _Pragma("unroll") for (int g = 0; g < FN; ++g) {                                                \
+    if ((RD) && 2 * g < 4 + FN) {                                                                 \
+      CH_READ(RBLK, RLO, WN_, AN_, 2 * g)                                                         \
+      if (2 * g + 1 < 4 + FN) CH_READ(RBLK, RLO, WN_, AN_, 2 * g + 1)                             \
+    }                                                                                             \
+    if ((LD) && g < 4) {                                                                          \
+      CH_LOAD(LT, 2 * g, LSO)                                                                     \
+      CH_LOAD(LT, 2 * g + 1, LSO)                                                                 \
+    }                                                                                             \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                 \
+      acc[g][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(WC[g], AC[j], acc[g][j], 0, 0, 0);        \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
   }
 
-  CH_DMA(0)
-  waitcnt<0, 15>();
-  barrier();
-  if (1 < NK) CH_DMA(1)
-  v4i wc[FN], ac[8];
-  CH_RD(0, wc, ac)
-  for (int t = 0; t < 2 * NK; ++t) {
-    if (t & 1) {
-      // step t+1 opens K block (t+1)/2, whose DMA was started two steps ago
-      waitcnt<0, 0>();
-      barrier();
-      if (((t + 1) >> 1) + 1 < NK) CH_DMA(((t + 1) >> 1) + 1)
-    }
-    v4i wn_[FN], an_[8];
-    CH_RD(t + 1, wn_, an_)
+  // prologue: block 0 loaded and visible, block 1 in flight
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+  for (int d = 0; d < 8; ++d) CH_LOAD(0, d, 0u)
+  wait_barrier<0, 15>();
+  {
+    const unsigned so1 = 1 < NK ? 0u : kChOob;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wc[i], ac[j], acc[i][j], 0, 0, 0);
-    // one LDS read for the next step after every 4 MFMAs (the last reads of
-    // a narrower tile trail the MFMAs)
-#pragma unroll
-    for (int g = 0; g < FN + 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ac[j] = an_[j];
-#pragma unroll
-    for (int i = 0; i < FN; ++i) wc[i] = wn_[i];
+    for (int d = 0; d < 8; ++d) CH_LOAD(1, d, so1)
   }
-#undef CH_DMA
-#undef CH_RD
-  // every load, and the loop's last (unused) look-ahead read, has landed
-  waitcnt<0, 0>();
-
+  v4i w0[FN], a0[4], w1[FN], a1[4];
+#pragma unroll
+  for (int r = 0; r < 4 + FN; ++r) CH_READ(0, lo0, w0, a0, r)
+  for (int kb = 0; kb + 1 < NK; ++kb) {
+    CH_STEP(w0, a0, true, kb, lo1, w1, a1, false, 0, 0u)
+    // block kb + 1 has landed everywhere; every wave is past its reads of kb
+    wait_barrier<0, 0>();
+    const unsigned so = kb + 2 < NK ? 0u : kChOob;
+    CH_STEP(w1, a1, true, kb + 1, lo0, w0, a0, true, kb + 2, so)
+  }
+  CH_STEP(w0, a0, true, NK - 1, lo1, w1, a1, false, 0, 0u)
+  // the epilogue's scales: for the bf16 channel-wise output they load under
+  // the last K step (the first fragment set is free by then, and all of the
+  // tile's stage loads were issued earlier, so the compiler's wait for these
+  // loads covers them too); the other epilogues hold more values per lane
+  // and load them after it
   const bool vec = (N & 3) == 0;
+  constexpr bool kEarly = OUT == OUT_BF16 && !AS;
+  float sam[4], swn[FN][4], zw[FN][4];
+  int wsx[FN][4];
+  auto load_scales = [&]() {
+    if (!AS) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + wm * 64 + j * 16 + (lane & 15);
+        sam[j] = m < M ? sa[m] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int n = n0 + wn * 16 * FN + i * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        swn[i][r] = n + r < N ? sw[n + r] : 0.f;
+        if (AS) wsx[i][r] = n + r < N ? wsum[n + r] : 0;
+      }
+    }
+  };
+  if (kEarly) load_scales();
+  CH_STEP(w1, a1, false, 0, 0, w0, a0, false, 0, 0u)
+#undef CH_LOAD
+#undef CH_READ
+#undef CH_STEP
+  // every stage load (the past-the-end ones included) has landed
+  waitcnt<0, 0>();
+  if (!kEarly && OUT != OUT_I32) load_scales();
+
   if (OUT == OUT_I32) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + wm * 128 + j * 16 + (lane & 15);
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + (lane & 15);
       if (m >= M) continue;
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
@@ -146,32 +210,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
     }
     return;
   }
-  // this lane's 8 activation scales and 8 x 4 weight scales, all loads in
-  // flight at once (asymmetric: per column fp32(s * sw), fp32(z * WS) and
-  // 128 WS instead)
-  float sam[8], swn[FN][4], zw[FN][4];
-  int wsx[FN][4];
-  if (!AS) {
+  if (AS) {
+    const float as_s = prm[0], as_z = prm[1];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + wm * 128 + j * 16 + (lane & 15);
-      sam[j] = m < M ? sa[m] : 0.f;
-    }
-  }
-  const float as_s = AS ? prm[0] : 0.f, as_z = AS ? prm[1] : 0.f;
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int n = n0 + wn * 16 * FN + i * 16 + 4 * (lane >> 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      swn[i][r] = n + r < N ? sw[n + r] : 0.f;
-      if (AS) {
-        const int ws = n + r < N ? wsum[n + r] : 0;
+      for (int r = 0; r < 4; ++r) {
         swn[i][r] = __fmul_rn(as_s, swn[i][r]);
-        zw[i][r] = __fmul_rn(as_z, (float)ws);
-        wsx[i][r] = 128 * ws;
+        zw[i][r] = __fmul_rn(as_z, (float)wsx[i][r]);
+        wsx[i][r] = 128 * wsx[i][r];
       }
-    }
   }
   // output value of accumulator r of fragment (i, j)
   auto outv = [&](int i, int j, int r) -> float {
@@ -180,17 +228,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   };
   if (OUT == OUT_F32) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + wm * 128 + j * 16 + (lane & 15);
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + (lane & 15);
       if (m >= M) continue;
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
         const int n = n0 + wn * 16 * FN + i * 16 + 4 * (lane >> 4);
         if (n >= N) continue;
-        float o[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = outv(i, j, r);
-        store4<OUT_F32>(Y, (int64_t)m * N + n, n, N, vec, o[0], o[1], o[2], o[3]);
+        store4<OUT_F32>(Y, (int64_t)m * N + n, n, N, vec, outv(i, j, 0), outv(i, j, 1), outv(i, j, 2),
+                        outv(i, j, 3));
       }
     }
     return;
@@ -202,8 +248,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   // touches, and the chunks a row read touches, fall in distinct bank groups.
   barrier();
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wm * 128 + j * 16 + (lane & 15);
+  for (int j = 0; j < 4; ++j) {
+    const int r = wm * 64 + j * 16 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
       uint32_t h[4];
@@ -216,22 +262,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_channel(const int8_t* __restric
   }
   waitcnt<63, 0>();
   barrier();
-  // wave w stores tile rows 64 w .. 64 w + 63, two rows per instruction;
+  // wave w stores tile rows 32 w .. 32 w + 31, two rows per instruction;
   // lane: row half lane >> 5, columns 8 (lane & 31) .. + 7 (chunks past the
-  // tile's BN columns are skipped)
+  // tile's BN columns are skipped).  The output is written once and not read
+  // back by this kernel: non-temporal stores.
   const int cl = lane & 31;
   const int n = n0 + 8 * cl;
   const bool vec8 = (N & 7) == 0 && n + 7 < N;
   const bool inside = cl < 4 * FN;
 #pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int r = wave * 64 + 2 * it + (lane >> 5);
+  for (int it = 0; it < 16; ++it) {
+    const int r = wave * 32 + 2 * it + (lane >> 5);
     const int m = m0 + r;
     const v4i v = *reinterpret_cast<const v4i*>(smem + r * 512 + ((cl ^ (r & 15)) << 4));
     if (m >= M || n >= N || !inside) continue;
     uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)m * N + n;
     if (vec8) {
-      *reinterpret_cast<v4i*>(y) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(y));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -273,6 +320,10 @@ __global__ __launch_bounds__(256) void k_splitk_sum_i32(const int32_t* __restric
 
 
 
+// Height in row tiles of the strips the channel tile kernel walks (the whole
+// column of row tiles when there are fewer than 8).
+int channel_strip(int TM) { return TM < 8 ? TM : 8; }
+
 // Tile width of the unsplit channel GEMM: FN 16-column fragments per wave
 // (BN = 32 FN) in {8, 7, 6}, the smallest modelled time, where a tile costs
 // per K block ~2960 FN / 8 cycles of MFMA issue and fragment reads plus
@@ -296,19 +347,20 @@ template <int FN>
 hipError_t channel_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, OutKind out,
                           int64_t M, int64_t N, int64_t K, int TM, hipStream_t st) {
   const int TN = (int)((N + 32 * FN - 1) / (32 * FN));
-  const dim3 grid((unsigned)(TM * TN)), block(256);
+  const dim3 grid((unsigned)(TM * TN)), block(512);
+  const int GM = channel_strip(TM);
   switch (out) {
     case OUT_BF16:
       hipLaunchKernelGGL((k_gemm_channel<OUT_BF16, FN>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K,
-                         TM);
+                         TM, GM);
       break;
     case OUT_F32:
       hipLaunchKernelGGL((k_gemm_channel<OUT_F32, FN>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K,
-                         TM);
+                         TM, GM);
       break;
     default:
       hipLaunchKernelGGL((k_gemm_channel<OUT_I32, FN>), grid, block, 0, st, A, sa, W, sw, Y, (int)M, (int)N, (int)K,
-                         TM);
+                         TM, GM);
       break;
   }
   return hipGetLastError();
@@ -319,13 +371,14 @@ hipError_t channel_asym_launch(const int8_t* A, const float* prm, const int8_t* 
                                const int32_t* wsum, void* Y, OutKind out, int64_t M, int64_t N, int64_t K, int TM,
                                hipStream_t st) {
   const int TN = (int)((N + 32 * FN - 1) / (32 * FN));
-  const dim3 grid((unsigned)(TM * TN)), block(256);
+  const dim3 grid((unsigned)(TM * TN)), block(512);
+  const int GM = channel_strip(TM);
   if (out == OUT_F32)
     hipLaunchKernelGGL((k_gemm_channel<OUT_F32, FN, true>), grid, block, 0, st, A, nullptr, W, sw, Y, (int)M,
-                       (int)N, (int)K, TM, prm, wsum);
+                       (int)N, (int)K, TM, GM, prm, wsum);
   else
     hipLaunchKernelGGL((k_gemm_channel<OUT_BF16, FN, true>), grid, block, 0, st, A, nullptr, W, sw, Y, (int)M,
-                       (int)N, (int)K, TM, prm, wsum);
+                       (int)N, (int)K, TM, GM, prm, wsum);
   return hipGetLastError();
 }
 
@@ -428,8 +481,8 @@ hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W
     void* ws = nullptr;
     hipError_t e = split_workspace(st, (size_t)S * M * N * 4, &ws);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(256), 0, st, A, sa,
-                       W, sw, ws, (int)M, (int)N, (int)K, TM);
+    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(512), 0, st, A, sa,
+                       W, sw, ws, (int)M, (int)N, (int)K, TM, channel_strip(TM));
     const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
     const int32_t* wsi = static_cast<const int32_t*>(ws);
     switch (out) {

@@ -31,6 +31,15 @@ __device__ __forceinline__ void waitcnt() {
 // Workgroup barrier that the compiler may not move memory accesses across.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt and s_barrier as one statement with a memory clobber: the
+// scheduler can move no LDS read of this wave below the wait (the
+// s_waitcnt builtin alone does not order memory accesses), so every read
+// issued before it has completed when the barrier releases the other waves.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(%1)\n\ts_barrier" ::"n"(VM), "n"(LGKM) : "memory");
+}
+
 // Raw buffer descriptor: base, no stride, `bytes` valid bytes.
 __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;

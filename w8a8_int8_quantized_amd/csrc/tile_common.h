@@ -62,5 +62,21 @@ __device__ __forceinline__ void xcd_tile(int b, int TM, int TN, int& tm, int& tn
   tn = t / TM;
 }
 
+// The same band of the tile sequence per XCD, with the sequence walking
+// strips of GM row tiles (m fastest inside a strip): an XCD's 32 concurrent
+// workgroups then cover about GM row tiles x 32 / GM column tiles and share
+// both operands' panels in its L2.  GM = TM is xcd_tile's order.
+__device__ __forceinline__ void strip_tile(int b, int TM, int TN, int GM, int& tm, int& tn) {
+  const int T = TM * TN;
+  const int x = b & 7, j = b >> 3;
+  const int T8 = T >> 3, rem = T & 7;
+  const int t = x * T8 + (x < rem ? x : rem) + j;
+  const int strip = t / (GM * TN);
+  const int r = t - strip * GM * TN;
+  const int gm = TM - strip * GM < GM ? TM - strip * GM : GM;
+  tm = strip * GM + r % gm;
+  tn = r / gm;
+}
+
 }  // namespace
 }  // namespace w8
