@@ -12,10 +12,10 @@
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  Calls
- *     are thread-safe.  The only state the library keeps is a split-K
- *     workspace per (device, stream) for gemm_w8a8_block, gemm_w8a8_channel,
- *     gemm_w8a16_group and the linear_* calls (described at
- *     gemm_w8a8_block), and one for quant_act_asym and gemm_w8a8_asym;
+ *     are thread-safe.  The only state the library keeps is its own scratch
+ *     (described at gemm_w8a8_block): a split-K workspace per (device,
+ *     stream) for gemm_w8a8_block, gemm_w8a8_channel, gemm_w8a16_group and
+ *     the linear_* calls, and one for quant_act_asym and gemm_w8a8_asym;
  *     every other entry point allocates nothing.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream) and returns without synchronising.
@@ -51,7 +51,9 @@ enum w8_status {
   W8_ERR_ALIGN = -3,  /* a pointer is not aligned as required */
   W8_ERR_DTYPE = -4,  /* unsupported dtype code */
   W8_ERR_LAUNCH = -5, /* the HIP runtime rejected a kernel launch or a workspace allocation */
-  W8_ERR_WORKSPACE = -6 /* a caller-provided workspace is smaller than required */
+  W8_ERR_WORKSPACE = -6, /* a caller-provided workspace is smaller than required */
+  W8_ERR_CAPTURE = -7  /* the call would allocate its scratch while its stream is being captured
+                          into a graph; nothing was enqueued */
 };
 
 enum w8_dtype { W8_BF16 = 0, W8_FP16 = 1, W8_FP32 = 2, W8_I32 = 3 };
@@ -132,13 +134,22 @@ int requant_fp8_to_int8_channel(const uint8_t* w_fp8, const float* scale_inv,
  * Split-K workspace (this call and gemm_w8a8_channel): when the output tile
  * grid is too small to occupy the GPU (few tiles of 256 x 256 for M > 128,
  * or 128 x 256 for M <= 128 block-wise), K is split into S slices whose
- * partial tiles (S x M x N x 4 bytes) go to a device workspace that the
- * library allocates on the first such call on a stream and grows when a
- * later call needs more (the growth synchronises that stream); it is kept
- * until the process ends.  The slices are summed in slice order, so results
- * stay deterministic.  A caller that captures graphs should make one such
- * call of the largest shape before capturing.  An allocation failure
- * returns W8_ERR_LAUNCH with nothing enqueued.
+ * partial tiles (S x M x N x 4 bytes) go to a device buffer that the library
+ * keeps per (device, stream).  It is allocated on the first such call on a
+ * stream; a later call that needs more gets a new buffer (size rounded up to
+ * a power of two) and the old one is retired, never freed while the process
+ * runs, since kernels enqueued earlier (or a graph captured with its
+ * address) may still use it.  Nothing synchronises.  A call holds the
+ * library's lock from taking its buffer until its kernels are enqueued, so
+ * host threads sharing a stream enqueue their sequences one after the other.
+ * The slices are summed in slice order, so results stay deterministic.
+ * While the stream is being captured into a graph the library allocates
+ * nothing: a call whose buffer would have to be allocated or grown returns
+ * W8_ERR_CAPTURE with nothing enqueued (make one call of the largest shape
+ * on the stream before capturing; the captured graph then uses that
+ * stream's buffer, and replaying it while other calls run on that stream
+ * races with them).  An allocation failure returns W8_ERR_LAUNCH with
+ * nothing enqueued.
  */
 int gemm_w8a8_block(const int8_t* A, const float* a_scale,
                     const int8_t* W, const float* w_scale,

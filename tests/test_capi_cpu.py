@@ -13,7 +13,7 @@ import w8a8_int8_quantized_amd as w8
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w8a8.h")
 
-OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS = 0, -1, -2, -3, -4, -6
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, ECAP = 0, -1, -2, -3, -4, -6, -7
 P16 = ctypes.c_void_p(1 << 20)        # a 16-byte aligned fake address (never dereferenced)
 P4 = ctypes.c_void_p((1 << 20) + 4)   # 4-byte but not 16-byte aligned
 NUL = ctypes.c_void_p(0)
@@ -35,8 +35,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert w8.lib.w8_abi_version() == 1
-    for rc in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, -5, EWS):
+    assert w8.lib.w8_abi_version() == 2
+    for rc in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, -5, EWS, ECAP):
         assert len(w8.lib.w8_status_string(rc)) > 0
     assert w8.lib.w8_status_string(99) == b"unknown status"
 

@@ -480,3 +480,35 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for o, r in zip(outs, ref):
             assert torch.equal(o.view(torch.int32), r.view(torch.int32)), rep
+
+
+def test_split_k_under_capture_without_workspace_is_refused():
+    """A stream being captured gets no allocation: a split-K call whose
+    stream has no workspace yet returns W8_ERR_CAPTURE with nothing enqueued
+    (the capture stays valid and records nothing); after one eager call on
+    that stream the same call captures and replays to the eager bits."""
+    M, N, K = 300, 1000, 4096        # small tile grid: K is split
+    qt, st = quant.quant_act_token(synth.to_numpy(synth.activations(M, K, seed=190)))
+    qc, sc = quant.quant_act_token(synth.to_numpy(synth.weights(N, K, seed=191)))
+    AT, ST, WC, SC = (torch.from_numpy(a).to(DEV) for a in (qt, st, qc, sc))
+    y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(w8.W8Error) as ei:
+        with torch.cuda.graph(g, stream=s):
+            w8.gemm_w8a8_channel(AT, ST, WC, SC, out=y)
+    assert ei.value.status == w8.W8_ERR_CAPTURE
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ref = w8.gemm_w8a8_channel(AT, ST, WC, SC, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=s):
+        w8.gemm_w8a8_channel(AT, ST, WC, SC, out=y)
+    for rep in range(2):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), rep

@@ -88,13 +88,18 @@ def _load():
 lib = _load()
 
 
+W8_ERR_WORKSPACE, W8_ERR_CAPTURE = -6, -7
+
+
 class W8Error(RuntimeError):
-    pass
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
 
 
 def _check(rc, what):
     if rc != 0:
-        raise W8Error(f"{what}: {lib.w8_status_string(rc).decode()} (status {rc})")
+        raise W8Error(f"{what}: {lib.w8_status_string(rc).decode()} (status {rc})", rc)
 
 
 def _stream():

@@ -182,9 +182,11 @@ hipError_t launch_quant_asym(const void* x, bool fp16, int64_t M, int64_t K, int
   const int64_t nchunks = M * K / 8;
   int64_t g = (nchunks + 4 * 256 - 1) / (4 * 256);
   const int wgs = (int)(g < kAsymMaxWgs ? g : kAsymMaxWgs);
-  void* part = nullptr;
-  hipError_t e = stream_workspace(st, 1, (size_t)wgs * 2 * sizeof(float), &part);
-  if (e != hipSuccess) return e;
+  // the partial ranges live in the stream's slot-1 scratch, held until both
+  // passes are enqueued
+  const WsLease lease = stream_workspace(st, 1, (size_t)wgs * 2 * sizeof(float));
+  if (lease.status() != kWsOk) return ws_error(lease);
+  void* part = lease.ptr();
   const uint4* xp = static_cast<const uint4*>(x);
   float* pp = static_cast<float*>(part);
   if (fp16) {
@@ -209,10 +211,12 @@ hipError_t launch_gemm_asym(const int8_t* A, const float* params, const int8_t* 
                             const int32_t* wsum, void* Y, OutKind out, int64_t M, int64_t N, int64_t K,
                             hipStream_t st) {
   if (channel_tiles_unsplit(M, N, K)) return launch_gemm_channel_asym_tiles(A, params, W, sw, wsum, Y, out, M, N, K, st);
-  void* acc = nullptr;
-  hipError_t e = stream_workspace(st, 1, (size_t)M * N * 4, &acc);
-  if (e != hipSuccess) return e;
-  e = launch_gemm_channel(A, nullptr, W, nullptr, acc, OUT_I32, M, N, K, st);
+  // int32 accumulators in the stream's slot-1 scratch, held until the
+  // epilogue is enqueued (the GEMM may take slot 0 inside it)
+  const WsLease lease = stream_workspace(st, 1, (size_t)M * N * 4);
+  if (lease.status() != kWsOk) return ws_error(lease);
+  void* acc = lease.ptr();
+  hipError_t e = launch_gemm_channel(A, nullptr, W, nullptr, acc, OUT_I32, M, N, K, st);
   if (e != hipSuccess) return e;
   const dim3 g((unsigned)((M * ((N + 3) / 4) + 255) / 256));
   const int32_t* ap = static_cast<const int32_t*>(acc);

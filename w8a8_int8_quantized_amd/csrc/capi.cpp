@@ -1,8 +1,10 @@
 // extern "C" entry points of libw8a8.so (declared in include/w8a8.h).
 //
-// This layer only validates arguments and dispatches to the launchers; it
-// allocates nothing and never synchronises.  Every check runs on the host
-// before anything is enqueued, so a failed call leaves the stream untouched.
+// This layer only validates arguments and dispatches to the launchers; every
+// check runs on the host before anything is enqueued, so a failed check
+// leaves the stream untouched.  The launchers of the split-K and asymmetric
+// paths take the library's per-stream scratch (csrc/workspace.h), which may
+// allocate on first use or growth; nothing here or there synchronises.
 #include <hip/hip_runtime.h>
 
 #include "../../include/w8a8.h"
@@ -10,7 +12,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
@@ -24,7 +26,14 @@ int check_rows_k(int64_t R, int64_t K) {
   return W8_OK;
 }
 
-int status_of(hipError_t e) { return e == hipSuccess ? W8_OK : W8_ERR_LAUNCH; }
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return W8_OK;
+  if (e == hipErrorStreamCaptureUnsupported) {
+    (void)hipGetLastError();
+    return W8_ERR_CAPTURE;
+  }
+  return W8_ERR_LAUNCH;
+}
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -67,6 +76,9 @@ const char* w8_status_string(int status) {
     case W8_ERR_DTYPE: return "unsupported dtype";
     case W8_ERR_LAUNCH: return "kernel launch or workspace allocation failed";
     case W8_ERR_WORKSPACE: return "caller-provided workspace too small";
+    case W8_ERR_CAPTURE:
+      return "the call would allocate its scratch while its stream is being captured "
+             "(make one call of the largest shape on the stream before capturing)";
     default: return "unknown status";
   }
 }

@@ -328,11 +328,10 @@ hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, 
   // ~2.6 us per 256 x 256 tile and K block (1.7 for 128 x 256) at the
   // measured large-M rate
   const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, BM == 256 ? 2.6 : 1.7);
-  void* dst = Y;
-  if (S > 1) {
-    hipError_t e = split_workspace(st, (size_t)S * M * N * 4, &dst);
-    if (e != hipSuccess) return e;
-  }
+  // a split K takes the stream's scratch, held until the reduction is enqueued
+  const WsLease lease = stream_workspace(st, 0, S > 1 ? (size_t)S * M * N * 4 : 0);
+  if (lease.status() != kWsOk) return ws_error(lease);
+  void* dst = S > 1 ? lease.ptr() : Y;
   const dim3 grid((unsigned)(TM * TN), (unsigned)S);
   const bool f32 = S > 1 || out == OUT_F32;
   if (BM == 128) {

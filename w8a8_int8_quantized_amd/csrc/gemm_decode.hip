@@ -1012,13 +1012,12 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s,
   while (wgs1 * S < target && S < 8 && KBt / (2 * S) >= 4) S *= 2;
   const int64_t wpc = nwv * ((wgs1 * S + kCUs - 1) / kCUs);
   const int pf = wpc <= 4 ? 8 : (wpc <= 8 ? 4 : 2);
-  float* part = nullptr;
-  if (S > 1 && M >= min_shared) {
-    void* p = nullptr;
-    const hipError_t e = split_workspace(st, (size_t)S * (M < 64 ? M : 64) * N * 4, &p);
-    if (e != hipSuccess) return e;
-    part = static_cast<float*>(p);
-  }
+  // slices' fp32 partials in the stream's scratch, held until every
+  // reduction below is enqueued
+  const bool split = S > 1 && M >= min_shared;
+  const WsLease lease = stream_workspace(st, 0, split ? (size_t)S * (M < 64 ? M : 64) * N * 4 : 0);
+  if (lease.status() != kWsOk) return ws_error(lease);
+  float* part = split ? static_cast<float*>(lease.ptr()) : nullptr;
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int mm = (int)(M - m0 < 64 ? M - m0 : 64);
     const uint16_t* xs = x + m0 * K;

@@ -12,7 +12,6 @@
 // accumulators are consecutive output columns n of one output row m:
 // contiguous stores and one activation scale per lane and fragment.
 #include <mutex>
-#include <vector>
 
 #include "tile_common.h"
 
@@ -384,21 +383,26 @@ hipError_t channel_asym_launch(const int8_t* A, const float* prm, const int8_t* 
 
 }  // namespace
 
-// Per-(device, stream, slot) workspaces, grown on demand and kept until the
-// process ends: slot 0 holds split-K partial tiles, slot 1 the asymmetric
-// GEMM's int32 accumulators and its quantiser's partial ranges (a GEMM there
-// may split K into slot 0 at the same time).  Calls on one stream are
-// ordered, so they may share a slot; different streams get different buffers.
-struct Workspace {
-  int dev;
-  hipStream_t st;
-  int slot;
-  void* p;
-  size_t bytes;
-};
+// The library's scratch buffers (workspace.h): device memory from hipMalloc,
+// never freed while the process runs (the cache itself is never destroyed,
+// so no HIP call runs during process teardown).
+bool HipScratch::alloc(void** p, size_t bytes) { return hipMalloc(p, bytes) == hipSuccess; }
+void HipScratch::release(void*) {}
+
 namespace {
-std::mutex g_ws_mu;
-std::vector<Workspace> g_ws;
+WorkspaceCache<HipScratch>& scratch_cache() {
+  static WorkspaceCache<HipScratch>* c = new WorkspaceCache<HipScratch>();
+  return *c;
+}
+
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs == hipStreamCaptureStatusActive;
+}
 }  // namespace
 
 // Number of K slices for a tile grid that leaves CUs idle: the smallest
@@ -421,43 +425,27 @@ int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_u
   return best;
 }
 
-hipError_t split_workspace(hipStream_t st, size_t bytes, void** out) { return stream_workspace(st, 0, bytes, out); }
-
-hipError_t stream_workspace(hipStream_t st, int slot, size_t bytes, void** out) {
+WsLease stream_workspace(hipStream_t st, int slot, size_t bytes) {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  for (Workspace& w : g_ws) {
-    if (w.dev == dev && w.st == st && w.slot == slot) {
-      if (w.bytes < bytes) {
-        // the stream's earlier kernels may still read the old buffer
-        e = hipStreamSynchronize(st);
-        if (e != hipSuccess) return e;
-        e = hipFree(w.p);
-        if (e != hipSuccess) return e;
-        w.p = nullptr;
-        w.bytes = 0;
-        e = hipMalloc(&w.p, bytes);
-        if (e != hipSuccess) return e;
-        w.bytes = bytes;
-      }
-      *out = w.p;
-      return hipSuccess;
-    }
-  }
-  void* p = nullptr;
-  e = hipMalloc(&p, bytes);
-  if (e != hipSuccess) return e;
-  g_ws.push_back({dev, st, slot, p, bytes});
-  *out = p;
-  return hipSuccess;
+  if (hipGetDevice(&dev) != hipSuccess) (void)hipGetLastError();
+  return scratch_cache().acquire(dev, reinterpret_cast<const void*>(st), slot, bytes, stream_capturing(st));
 }
+
+hipError_t ws_error(const WsLease& lease) {
+  switch (lease.status()) {
+    case kWsOk: return hipSuccess;
+    case kWsCapturing: return hipErrorStreamCaptureUnsupported;
+    default: return hipErrorOutOfMemory;
+  }
+}
+
+namespace {
+int channel_slices(int64_t M, int64_t N, int64_t K);
+}  // namespace
 
 bool channel_tiles_unsplit(int64_t M, int64_t N, int64_t K) {
   if (decode_path_takes(M, N, true)) return false;
-  const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + 255) / 256);
-  return pick_k_slices((int64_t)TM * TN, K >> 7, M, N, 2.2) == 1;
+  return channel_slices(M, N, K) == 1;
 }
 
 hipError_t launch_gemm_channel_asym_tiles(const int8_t* A, const float* prm, const int8_t* W, const float* sw,
@@ -471,39 +459,60 @@ hipError_t launch_gemm_channel_asym_tiles(const int8_t* A, const float* prm, con
   }
 }
 
-hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
-                               OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (decode_path_takes(M, N, true)) return launch_gemm_channel_decode(A, sa, W, sw, Y, out, M, N, K, st);
+namespace {
+
+// K slices of the channel tile grid for (M, N, K); 1 runs it unsplit.
+// ~1.6 us per 256 x 256 tile and K block at the measured large-M rate.
+int channel_slices(int64_t M, int64_t N, int64_t K) {
   const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + 255) / 256);
-  // ~2.2 us per 256 x 256 tile and K block at the measured large-M rate
-  const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, 2.2);
-  if (S > 1) {
-    void* ws = nullptr;
-    hipError_t e = split_workspace(st, (size_t)S * M * N * 4, &ws);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(512), 0, st, A, sa,
-                       W, sw, ws, (int)M, (int)N, (int)K, TM, channel_strip(TM));
-    const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
-    const int32_t* wsi = static_cast<const int32_t*>(ws);
-    switch (out) {
-      case OUT_BF16:
-        hipLaunchKernelGGL((k_splitk_sum_i32<OUT_BF16>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
-        break;
-      case OUT_F32:
-        hipLaunchKernelGGL((k_splitk_sum_i32<OUT_F32>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
-        break;
-      default:
-        hipLaunchKernelGGL((k_splitk_sum_i32<OUT_I32>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
-        break;
-    }
-    return hipGetLastError();
+  return pick_k_slices((int64_t)TM * TN, K >> 7, M, N, 1.6);
+}
+
+// The split-K path: S slices of 256 x 256 tiles write int32 partial tiles to
+// ws (S x M x N x 4 bytes), then one pass sums them in slice order and
+// applies the epilogue.
+hipError_t channel_split(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, OutKind out,
+                         int64_t M, int64_t N, int64_t K, int S, void* ws, hipStream_t st) {
+  const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + 255) / 256);
+  hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(512), 0, st, A, sa,
+                     W, sw, ws, (int)M, (int)N, (int)K, TM, channel_strip(TM));
+  const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
+  const int32_t* wsi = static_cast<const int32_t*>(ws);
+  switch (out) {
+    case OUT_BF16:
+      hipLaunchKernelGGL((k_splitk_sum_i32<OUT_BF16>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
+      break;
+    case OUT_F32:
+      hipLaunchKernelGGL((k_splitk_sum_i32<OUT_F32>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
+      break;
+    default:
+      hipLaunchKernelGGL((k_splitk_sum_i32<OUT_I32>), rg, dim3(256), 0, st, wsi, S, (int)M, (int)N, sa, sw, Y);
+      break;
   }
-  const int FN = pick_channel_width(TM, N);
-  switch (FN) {
+  return hipGetLastError();
+}
+
+hipError_t channel_tiles(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, OutKind out,
+                         int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int TM = (int)((M + kChBM - 1) / kChBM);
+  switch (pick_channel_width(TM, N)) {
     case 7: return channel_launch<7>(A, sa, W, sw, Y, out, M, N, K, TM, st);
     case 6: return channel_launch<6>(A, sa, W, sw, Y, out, M, N, K, TM, st);
     default: return channel_launch<8>(A, sa, W, sw, Y, out, M, N, K, TM, st);
   }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
+                               OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (decode_path_takes(M, N, true)) return launch_gemm_channel_decode(A, sa, W, sw, Y, out, M, N, K, st);
+  const int S = channel_slices(M, N, K);
+  if (S == 1) return channel_tiles(A, sa, W, sw, Y, out, M, N, K, st);
+  // the stream's scratch, held until both kernels are enqueued
+  const WsLease lease = stream_workspace(st, 0, (size_t)S * M * N * 4);
+  if (lease.status() != kWsOk) return ws_error(lease);
+  return channel_split(A, sa, W, sw, Y, out, M, N, K, S, lease.ptr(), st);
 }
 
 }  // namespace w8

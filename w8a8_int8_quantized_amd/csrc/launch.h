@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "workspace.h"
+
 namespace w8 {
 
 enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_I32 = 2 };
@@ -44,11 +46,20 @@ hipError_t launch_gemm_asym(const int8_t* A, const float* params, const int8_t* 
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
                              int64_t K, hipStream_t st);
 
-// Split-K workspace: at least `bytes` of device memory kept for `st` on the
-// current device (grown on demand; the growth synchronises `st`).
-hipError_t split_workspace(hipStream_t st, size_t bytes, void** out);
-// The same for workspace `slot` (0: split-K partials, 1: the asymmetric path).
-hipError_t stream_workspace(hipStream_t st, int slot, size_t bytes, void** out);
+// The library's own scratch (rules in workspace.h): at least `bytes` of
+// device memory for (current device, `st`, `slot`), slot 0 for split-K
+// partial tiles, slot 1 for the asymmetric path.  The lease holds the
+// library's lock: keep it until every kernel that uses the buffer has been
+// enqueued.  ws_error maps a failed lease to hipErrorOutOfMemory, or to
+// hipErrorStreamCaptureUnsupported when `st` is being captured and the
+// buffer would have to be allocated.
+struct HipScratch {
+  static bool alloc(void** p, size_t bytes);
+  static void release(void* p);
+};
+using WsLease = WorkspaceCache<HipScratch>::Lease;
+WsLease stream_workspace(hipStream_t st, int slot, size_t bytes);
+hipError_t ws_error(const WsLease& lease);
 // Number of K slices (1..16) for a grid of `tiles` workgroups over KB K
 // blocks, from a model with t_kb_us microseconds per tile and K block.
 int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us);
