@@ -15,8 +15,9 @@
  *     are thread-safe.  The only state the library keeps is its own scratch
  *     (described at gemm_w8a8_block): a split-K workspace per (device,
  *     stream) for gemm_w8a8_block, gemm_w8a8_channel, gemm_w8a16_group and
- *     the linear_* calls, and one for quant_act_asym and gemm_w8a8_asym;
- *     every other entry point allocates nothing.
+ *     the linear_* calls, one for quant_act_asym and gemm_w8a8_asym, and the
+ *     fixed array of gemm_w8a8_channel_noalloc; every other entry point
+ *     allocates nothing.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream) and returns without synchronising.
  *     Results are visible once the stream reaches that point.
@@ -51,7 +52,8 @@ enum w8_status {
   W8_ERR_ALIGN = -3,  /* a pointer is not aligned as required */
   W8_ERR_DTYPE = -4,  /* unsupported dtype code */
   W8_ERR_LAUNCH = -5, /* the HIP runtime rejected a kernel launch or a workspace allocation */
-  W8_ERR_WORKSPACE = -6, /* a caller-provided workspace is smaller than required */
+  W8_ERR_WORKSPACE = -6, /* a workspace is smaller than required (a caller-provided one, or the
+                            fixed scratch of gemm_w8a8_channel_noalloc) */
   W8_ERR_CAPTURE = -7  /* the call would allocate its scratch while its stream is being captured
                           into a graph; nothing was enqueued */
 };
@@ -173,6 +175,25 @@ int gemm_w8a8_channel(const int8_t* A, const float* a_scale,
                       const int8_t* W, const float* w_scale,
                       void* Y, int y_dtype, int64_t M, int64_t N, int64_t K,
                       void* stream);
+
+/*
+ * gemm_w8a8_channel for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results (bit-identical) as
+ * gemm_w8a8_channel; where that call would take its split-K workspace, this
+ * one uses a fixed scratch array of 64 MiB compiled into the library (each
+ * GPU the library runs on holds its own copy until the process ends).  It
+ * calls no allocating routine.  A shape whose split-K partial tiles
+ * (S x M x N x 4 bytes) exceed 64 MiB returns W8_ERR_WORKSPACE with nothing
+ * enqueued.  Every call of this entry point on one GPU shares that GPU's
+ * array: two calls that overlap in time on one GPU (on different streams,
+ * or replayed graphs) race and give wrong results; calls on one stream are
+ * ordered and safe.
+ */
+int gemm_w8a8_channel_noalloc(const int8_t* A, const float* a_scale,
+                              const int8_t* W, const float* w_scale,
+                              void* Y, int y_dtype, int64_t M, int64_t N,
+                              int64_t K, void* stream);
 
 /*
  * The int32 block partial sums of the block-wise GEMM, for bit-exact checks:

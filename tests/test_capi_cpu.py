@@ -79,6 +79,15 @@ def test_gemm_argument_checks():
     assert L.gemm_w8a8_channel(P16, NUL, P16, P16, P16, w8.W8_FP32, 4, 4, 128, NUL) == ENULL
     assert L.gemm_w8a8_channel(P16, P16, P16, P16, NUL, w8.W8_FP32, 4, 4, 128, NUL) == ENULL
     assert L.gemm_w8a8_channel(NUL, NUL, NUL, NUL, NUL, w8.W8_FP32, 4, 0, 128, NUL) == OK
+    # the allocation-free variant checks its arguments the same way
+    fn = L.gemm_w8a8_channel_noalloc
+    assert fn(P16, P16, P16, P16, P16, 9, 4, 4, 128, NUL) == EDTYPE
+    assert fn(P16, P16, P16, P16, P16, w8.W8_I32, 4, 4, 1 << 18, NUL) == ESHAPE
+    assert fn(P16, P16, P16, P16, P16, w8.W8_I32, 4, 4, 200, NUL) == ESHAPE
+    assert fn(P16, NUL, P16, P16, P16, w8.W8_FP32, 4, 4, 128, NUL) == ENULL
+    assert fn(P16, P16, P16, P16, NUL, w8.W8_FP32, 4, 4, 128, NUL) == ENULL
+    assert fn(P4, P16, P16, P16, P16, w8.W8_I32, 4, 4, 128, NUL) == EALIGN
+    assert fn(NUL, NUL, NUL, NUL, NUL, w8.W8_FP32, 0, 4, 128, NUL) == OK
     assert L.gemm_w8a8_block_partials(P16, P16, NUL, 4, 4, 128, NUL) == ENULL
     assert L.gemm_w8a8_block_partials(P16, P16, P16, 4, -4, 128, NUL) == ESHAPE
     assert L.gemm_w8a16_group(P16, P16, P16, P16, 4, 4, 96, NUL) == ESHAPE

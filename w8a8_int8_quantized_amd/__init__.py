@@ -49,6 +49,9 @@ _FUNCS = {
     "gemm_w8a8_channel": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_void_p]),
+    "gemm_w8a8_channel_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "gemm_w8a8_block_partials": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "gemm_w8a16_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -219,6 +222,19 @@ def gemm_w8a8_channel(A, a_scale, W, w_scale, out_dtype=torch.bfloat16, out=None
     y = out if out is not None else _empty((M, N), out_dtype, A)
     _check(lib.gemm_w8a8_channel(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(y), _out_code(y.dtype), M, N, K,
                                  _stream()), "gemm_w8a8_channel")
+    return y
+
+
+def gemm_w8a8_channel_noalloc(A, a_scale, W, w_scale, out_dtype=torch.bfloat16, out=None):
+    """gemm_w8a8_channel with its split-K partials in the library's fixed
+    64 MiB scratch array instead of an allocated workspace (for callers that
+    cannot allocate); pass `out` to allocate nothing here either."""
+    _dev(A, W, a_scale, w_scale)
+    M, K = A.shape
+    N = W.shape[0]
+    y = out if out is not None else _empty((M, N), out_dtype, A)
+    _check(lib.gemm_w8a8_channel_noalloc(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(y), _out_code(y.dtype), M, N,
+                                         K, _stream()), "gemm_w8a8_channel_noalloc")
     return y
 
 

@@ -75,7 +75,9 @@ const char* w8_status_string(int status) {
     case W8_ERR_ALIGN: return "misaligned pointer (data 16-byte, scales 4-byte)";
     case W8_ERR_DTYPE: return "unsupported dtype";
     case W8_ERR_LAUNCH: return "kernel launch or workspace allocation failed";
-    case W8_ERR_WORKSPACE: return "caller-provided workspace too small";
+    case W8_ERR_WORKSPACE:
+      return "workspace too small (a caller-provided workspace, or the 64 MiB fixed scratch of "
+             "gemm_w8a8_channel_noalloc)";
     case W8_ERR_CAPTURE:
       return "the call would allocate its scratch while its stream is being captured "
              "(make one call of the largest shape on the stream before capturing)";
@@ -163,6 +165,25 @@ int gemm_w8a8_channel(const int8_t* A, const float* a_scale, const int8_t* W, co
     if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
   }
   return status_of(w8::launch_gemm_channel(A, a_scale, W, w_scale, Y, out, M, N, K, as_stream(stream)));
+}
+
+int gemm_w8a8_channel_noalloc(const int8_t* A, const float* a_scale, const int8_t* W, const float* w_scale,
+                              void* Y, int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  w8::OutKind out;
+  int rc = check_out(y_dtype, true, &out);
+  if (rc) return rc;
+  rc = check_gemm_common(A, W, Y, M, N, K);
+  if (rc || M == 0 || N == 0) return rc;
+  if (K == 0 || K > (int64_t(1) << 17)) return W8_ERR_SHAPE;
+  if (out != w8::OUT_I32) {
+    if (!a_scale || !w_scale) return W8_ERR_NULL;
+    if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
+  }
+  bool too_big = false;
+  const hipError_t e =
+      w8::launch_gemm_channel_noalloc(A, a_scale, W, w_scale, Y, out, M, N, K, as_stream(stream), &too_big);
+  if (too_big) return W8_ERR_WORKSPACE;
+  return status_of(e);
 }
 
 int gemm_w8a8_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,

@@ -515,4 +515,53 @@ hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W
   return channel_split(A, sa, W, sw, Y, out, M, N, K, S, lease.ptr(), st);
 }
 
+// ------------------------------------------------- allocation-free variant
+// The scratch of gemm_w8a8_channel_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, kept until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the array's
+// device address on the current GPU comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to kernels.
+constexpr size_t kFixedScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kFixedScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_fixed_mu;
+void* g_fixed_ptr[kMaxDevices] = {};
+
+// The array's address on the current device (looked up on the device's
+// first call, with that device current).
+hipError_t fixed_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_fixed_mu);
+  if (!g_fixed_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_fixed_ptr[dev] = p;
+  }
+  *out = g_fixed_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_gemm_channel_noalloc(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
+                                       OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st, bool* too_big) {
+  *too_big = false;
+  if (decode_path_takes(M, N, true)) return launch_gemm_channel_decode(A, sa, W, sw, Y, out, M, N, K, st);
+  const int S = channel_slices(M, N, K);
+  if (S == 1) return channel_tiles(A, sa, W, sw, Y, out, M, N, K, st);
+  if ((size_t)S * M * N * 4 > kFixedScratchBytes) {
+    *too_big = true;
+    return hipErrorInvalidValue;
+  }
+  void* ws = nullptr;
+  const hipError_t e = fixed_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return channel_split(A, sa, W, sw, Y, out, M, N, K, S, ws, st);
+}
+
 }  // namespace w8

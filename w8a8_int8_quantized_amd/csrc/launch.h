@@ -22,6 +22,11 @@ hipError_t launch_requant_channel(const uint8_t* w, const float* si, int64_t N, 
 
 hipError_t launch_gemm_channel(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                                OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+// launch_gemm_channel with the split-K partials in the library's fixed
+// scratch array instead of the per-stream workspace: allocates nothing.  A
+// split whose partials exceed the array sets *too_big and enqueues nothing.
+hipError_t launch_gemm_channel_noalloc(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
+                                       OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st, bool* too_big);
 hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                              OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
