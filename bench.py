@@ -18,6 +18,8 @@ cannot serve repeats, the grouped MoE GEMMs, and the FP8 requantisation.
 
 roofline: the dominant kernel (the gate_up channel GEMM), timed with HIP
 events on the stream it runs on, against the dense int8 MFMA peak of 5.0 POP/s.
+clock: the GFX clocks and socket power that amd-smi reports while the gate_up
+GEMM runs back to back for about two seconds (the MFMA peak assumes 2.4 GHz).
 cpu_baseline: the CPU oracle (numpy) on a bounded sample of the same step.
 """
 
@@ -39,7 +41,7 @@ DOWN = (18432, 7168)
 # traffic of the dominant kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
 # scaled by the same counters' reading for a copy kernel of known size; None
 # until counters have been taken for the current kernel.
-TRAFFIC_GATE_UP_BYTES = 2.694e9   # rocprofv3 FETCH_SIZE x2.000 + WRITE_SIZE x1.000 (copy-calibrated), per launch
+TRAFFIC_GATE_UP_BYTES = 1.889e9   # rocprofv3 FETCH_SIZE x2.000 + WRITE_SIZE x1.000 (copy-calibrated), per launch of the current kernel
 
 
 def parse():
@@ -52,6 +54,7 @@ def parse():
     ap.add_argument("--rows-reps", type=int, default=20)
     ap.add_argument("--rows-only", default="",
                     help="comma list of row groups to run: quant,tile,decode,w8a16,moe (default all)")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock window")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the reference kernel of known "
                          "size for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -138,6 +141,92 @@ def headline(args):
     return ms, tops, k_ms, k_tops, parts
 
 
+def _smi_sample():
+    """GFX clocks (MHz, one per XCD) and socket power (W) from amd-smi."""
+    import re
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if exe is None:
+        return None
+    try:
+        txt = subprocess.run([exe, "metric", "-g", "0", "-c", "-p"], capture_output=True, text=True,
+                             timeout=20).stdout
+    except Exception:                                           # pragma: no cover
+        return None
+    clocks, power, in_gfx = [], None, False
+    for line in txt.splitlines():
+        t = line.strip()
+        if re.match(r"GFX_\d+:", t):
+            in_gfx = True
+        elif re.match(r"[A-Z]+_\d+:", t) or t.startswith("MEM"):
+            in_gfx = False
+        m = re.match(r"CLK:\s*(\d+)\s*MHz", t)
+        if m and in_gfx:
+            clocks.append(int(m.group(1)))
+        m = re.match(r"SOCKET_POWER:\s*(\d+)", t)
+        if m:
+            power = int(m.group(1))
+    return (clocks, power) if clocks else None
+
+
+def clock_window(seconds=4.0):
+    """The gate_up GEMM back to back for about `seconds` while a thread
+    samples amd-smi three times inside that window: mean GFX clock, socket
+    power, and the GEMM's rate in the same window."""
+    import threading
+    import torch
+    import synth
+    import w8a8_int8_quantized_amd as w8
+    dev = torch.device("cuda:0")
+    (K, N) = GATE_UP
+    qa = w8.quant_act_token(synth.activations(M_HEAD, K, seed=synth.SEEDS["channel"], device=dev))
+    wq = w8.quant_act_token(synth.weights(N, K, seed=synth.SEEDS["channel"] + 20, device=dev))
+    y = torch.empty(M_HEAD, N, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        w8.gemm_w8a8_channel(qa[0], qa[1], wq[0], wq[1], out=y)
+    torch.cuda.synchronize()
+    a, b = _events()
+    a.record()
+    w8.gemm_w8a8_channel(qa[0], qa[1], wq[0], wq[1], out=y)
+    b.record()
+    torch.cuda.synchronize()
+    n = max(1, int(seconds / max(a.elapsed_time(b) * 1e-3, 1e-4)))
+    samples = []
+
+    def sampler():
+        time.sleep(0.5)
+        for _ in range(3):
+            r = _smi_sample()
+            if r is not None:
+                samples.append(r)
+            time.sleep(0.3)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    a.record()
+    for _ in range(n):
+        w8.gemm_w8a8_channel(qa[0], qa[1], wq[0], wq[1], out=y)
+    b.record()
+    th.join()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    del qa, wq, y
+    torch.cuda.empty_cache()
+    out = {"gate_up_ms": round(ms, 4), "gate_up_tops": round(2.0 * M_HEAD * N * K / ms / 1e9, 1),
+           "window_s": round(ms * n / 1e3, 2)}
+    if not samples:
+        out["source"] = "amd-smi unavailable"
+        return out
+    clocks = [c for cl, _ in samples for c in cl]
+    powers = [p for _, p in samples if p is not None]
+    out.update({"source": "amd-smi metric -c -p, 3 samples while the gate_up GEMM runs back to back",
+                "gfx_mhz_mean": round(sum(clocks) / len(clocks)), "gfx_mhz_min": min(clocks),
+                "gfx_mhz_max": max(clocks),
+                "socket_power_w": round(sum(powers) / len(powers)) if powers else None})
+    return out
+
+
 def rows(args):
     """Every other row of the path at its own shapes."""
     import torch
@@ -161,16 +250,23 @@ def rows(args):
         return groups is None or g in groups
 
     if want("quant"):
-        # --- quantisers at M = 4096, K = 7168 (bytes: 2 in + 1 out + scales)
-        x = synth.activations(4096, 7168, seed=2, device=dev)
-        ms = time_calls(lambda i: w8.quant_act_group(x), 1, R)
+        # --- quantisers at M = 4096, K = 7168 (bytes: 2 in + 1 out + scales),
+        # 12 input and output copies (1.06 GB) rotated
+        NQ = 12
+        xs = [synth.activations(4096, 7168, seed=2 + i, device=dev) for i in range(NQ)]
+        qs = [torch.empty(4096, 7168, dtype=torch.int8, device=dev) for _ in range(NQ)]
+        sg = [torch.empty(4096, 56, dtype=torch.float32, device=dev) for _ in range(NQ)]
+        st_ = [torch.empty(4096, dtype=torch.float32, device=dev) for _ in range(NQ)]
+        ms = time_calls(lambda i: w8.quant_act_group(xs[i], out=(qs[i], sg[i])), NQ, R)
         b = 4096 * 7168 * 3 + 4096 * 56 * 4
         out["quant_act_group_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
                                             "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
-        ms = time_calls(lambda i: w8.quant_act_token(x), 1, R)
+        ms = time_calls(lambda i: w8.quant_act_token(xs[i], out=(qs[i], st_[i])), NQ, R)
         b = 4096 * 7168 * 3 + 4096 * 4
         out["quant_act_token_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
                                             "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+        del xs, qs, sg, st_
+        torch.cuda.empty_cache()
 
     if want("tile"):
         # --- block-wise at M = 4096 (DeepSeek-V3 shapes), weights FP8 -> requantised
@@ -179,10 +275,15 @@ def rows(args):
             K, N = synth.SHAPES[name]
             codes, si = synth.fp8_weights(N, K, seed=synth.SEEDS["block"], device=dev)
             if name == "gate_up":
-                ms = time_calls(lambda i: w8.requant_fp8_to_int8_block(codes, si), 1, 5)
+                # two sets of codes and outputs rotated (2 x 529 MB of traffic per pair of calls)
+                codes2 = [codes, synth.fp8_weights(N, K, seed=synth.SEEDS["block"] + 50, device=dev)[0]]
+                outs2 = [(torch.empty(N, K, dtype=torch.int8, device=dev),
+                          torch.empty((N + 127) // 128, K // 128, dtype=torch.float32, device=dev)) for _ in range(2)]
+                ms = time_calls(lambda i: w8.requant_fp8_to_int8_block(codes2[i], si, out=outs2[i]), 2, 6)
                 b = N * K * 2
                 out["requant_fp8_block_gate_up"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
                                                     "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
+                del codes2, outs2
             wq, ws = w8.requant_fp8_to_int8_block(codes, si)
             del codes
             if K not in qa_cache:
@@ -195,15 +296,19 @@ def rows(args):
             out[f"gemm_block_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
             if name in ("gate_up", "down"):
                 qt = w8.quant_act_token(synth.activations(4096, K, seed=5, device=dev))
-                wqc, wsc = w8.quant_act_token(synth.weights(N, K, seed=6, device=dev))
-                ms = time_calls(lambda i: w8.gemm_w8a8_channel(qt[0], qt[1], wqc, wsc, out=y), 1, max(5, R // 2))
+                # weight copies rotated through more than 1 GB (4 of gate_up's
+                # 264 MB, 8 of down's 132 MB): the M = 128 rows are HBM-bound
+                nrot = 4 if name == "gate_up" else 8
+                wcs = [w8.quant_act_token(synth.weights(N, K, seed=6 + i, device=dev)) for i in range(nrot)]
+                ms = time_calls(lambda i: w8.gemm_w8a8_channel(qt[0], qt[1], wcs[i][0], wcs[i][1], out=y), nrot,
+                                max(5, R // 2))
                 out[f"gemm_channel_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
                 for M in (128, 1024):
                     yq = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
                     a0, a1 = qt[0][:M].contiguous(), qt[1][:M].contiguous()
-                    ms = time_calls(lambda i: w8.gemm_w8a8_channel(a0, a1, wqc, wsc, out=yq), 1, R)
+                    ms = time_calls(lambda i: w8.gemm_w8a8_channel(a0, a1, wcs[i][0], wcs[i][1], out=yq), nrot, R)
                     out[f"gemm_channel_m{M}_{name}"] = gemm_entry(ms, M, N, K, N * K)
-                del wqc, wsc, qt
+                del wcs, qt
             del wq, ws, y
         del qa_cache
         torch.cuda.empty_cache()
@@ -235,22 +340,27 @@ def rows(args):
         # algorithmic bytes 2 in + 1 out per element) and the GEMM at 4096 rows
         # and one row, gate_up shape, per-channel weights
         K, N = GATE_UP
-        x = synth.activations(4096, K, seed=7, device=dev)
-        ms = time_calls(lambda i: w8.quant_act_asym(x), 1, R)
+        xs = [synth.activations(4096, K, seed=7 + i, device=dev) for i in range(12)]
+        ms = time_calls(lambda i: w8.quant_act_asym(xs[i]), 12, R)
+        x = xs[0]
+        del xs[1:]
         b = 4096 * K * 3
         out["quant_act_asym_4096x7168"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
                                            "hbm_frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 3)}
         qa, prm = w8.quant_act_asym(x)
-        wq, wsc = w8.quant_act_token(synth.weights(N, K, seed=8, device=dev))
-        wsum = w8.weight_row_sums(wq)
+        # four weight copies (1.06 GB) rotated: the one-row GEMM is HBM-bound
+        wts = []
+        for i in range(4):
+            wq, wsc = w8.quant_act_token(synth.weights(N, K, seed=8 + i, device=dev))
+            wts.append((wq, wsc, w8.weight_row_sums(wq)))
         y = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: w8.gemm_w8a8_asym(qa, prm, wq, wsc, wsum, out=y), 1, max(5, R // 2))
+        ms = time_calls(lambda i: w8.gemm_w8a8_asym(qa, prm, *wts[i], out=y), 4, max(5, R // 2))
         out["gemm_asym_m4096_gate_up"] = gemm_entry(ms, 4096, N, K, N * K)
         y1 = torch.empty(1, N, dtype=torch.bfloat16, device=dev)
         a1 = qa[:1].contiguous()
-        ms = time_calls(lambda i: w8.gemm_w8a8_asym(a1, prm, wq, wsc, wsum, out=y1), 1, R)
+        ms = time_calls(lambda i: w8.gemm_w8a8_asym(a1, prm, *wts[i], out=y1), 4, R)
         out["decode_asym_m1_gate_up"] = gemm_entry(ms, 1, N, K, N * K + 8 * N)
-        del x, qa, wq, y
+        del x, qa, wts, y
         torch.cuda.empty_cache()
 
     if want("w8a16"):
@@ -403,6 +513,10 @@ def main():
     ms, tops, k_ms, k_tops, parts = headline(args)
     print(f"[bench] headline {ms:.3f} ms/step, {tops:.1f} TOPS; gate_up kernel {k_ms:.3f} ms", file=sys.stderr,
           flush=True)
+    clock = None
+    if not args.no_clock:
+        print("[bench] clock window", file=sys.stderr, flush=True)
+        clock = clock_window()
     extra = {}
     if not args.no_rows:
         print("[bench] rows", file=sys.stderr, flush=True)
@@ -430,9 +544,11 @@ def main():
                                "(K=7168 -> N=36864) + per-token quant + down (K=18432 -> N=7168)",
                    "M": M_HEAD, "gate_up": [Kg, Ng], "down": list(DOWN), "out_dtype": "bf16",
                    "parallelism": "1 GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(k_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": round(k_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                      "frac": round(k_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                     "kernel": "gemm_w8a8_channel gate_up M=4096", "kernel_ms": round(k_ms, 4)},
+                     "kernel": "gemm_w8a8_channel gate_up M=4096", "kernel_ms": round(k_ms, 4),
+                     "peak_note": "dense int8 MFMA, 5.0 POP/s at 2.4 GHz (int8 ops, not flops)"},
+        "clock": clock,
         "cpu_baseline": cpu,
         "step_parts_ms": parts,
         "rows": extra,

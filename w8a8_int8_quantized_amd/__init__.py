@@ -174,15 +174,17 @@ def quant_weight_channel(w):
     return quant_act_token(w)
 
 
-def requant_fp8_to_int8_block(w_fp8, scale_inv, return_bf16=False):
-    """FP8-E4M3FN codes [N, K] (uint8) with scale_inv [NB, KB] -> BF16 -> INT8 128x128 tiles."""
+def requant_fp8_to_int8_block(w_fp8, scale_inv, return_bf16=False, out=None):
+    """FP8-E4M3FN codes [N, K] (uint8) with scale_inv [NB, KB] -> BF16 -> INT8 128x128 tiles
+    (out: an optional (codes, scales) pair to write into)."""
     _dev(w_fp8, scale_inv)
     if w_fp8.dtype == torch.float8_e4m3fn:
         w_fp8 = w_fp8.view(torch.uint8)
     N, K = w_fp8.shape
     NB = (N + GROUP - 1) // GROUP
-    q = _empty((N, K), torch.int8, w_fp8)
-    s = _empty((NB, K // GROUP), torch.float32, w_fp8)
+    q, s = out if out is not None else (_empty((N, K), torch.int8, w_fp8), _empty((NB, K // GROUP), torch.float32,
+                                                                                 w_fp8))
+    _dev(q, s)
     wb = _empty((N, K), torch.bfloat16, w_fp8) if return_bf16 else None
     _check(lib.requant_fp8_to_int8_block(_p(w_fp8), _p(scale_inv), N, K, _p(q), _p(s), _p(wb), _stream()),
            "requant_fp8_to_int8_block")
