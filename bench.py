@@ -294,6 +294,17 @@ def rows(args):
             y = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
             ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wq, ws, out=y), 1, max(5, R // 2))
             out[f"gemm_block_m4096_{name}"] = gemm_entry(ms, 4096, N, K, N * K)
+            if name == "gate_up":
+                # the next layer's group quantisation fused into the epilogue,
+                # against the GEMM (bf16) followed by quant_act_group
+                qo = (torch.empty(4096, N, dtype=torch.int8, device=dev),
+                      torch.empty(4096, N // 128, dtype=torch.float32, device=dev))
+                ms_f = time_calls(lambda i: w8.gemm_w8a8_block_quant(qa, sa, wq, ws, out=qo), 1, max(5, R // 2))
+                ms_u = time_calls(lambda i: (w8.gemm_w8a8_block(qa, sa, wq, ws, out=y), w8.quant_act_group(y, out=qo)),
+                                  1, max(5, R // 2))
+                out["fused_block_quant_m4096_gate_up"] = {"ms": round(ms_f, 4), "unfused_ms": round(ms_u, 4),
+                                                          "TOPS": round(2.0 * 4096 * N * K / ms_f / 1e9, 1)}
+                del qo
             if name in ("gate_up", "down"):
                 qt = w8.quant_act_token(synth.activations(4096, K, seed=5, device=dev))
                 # weight copies rotated through more than 1 GB (4 of gate_up's
@@ -332,6 +343,14 @@ def rows(args):
             wsp = torch.empty(w8.linear_workspace_bytes(w8.W8_SCHEME_BLOCK, M, K), dtype=torch.uint8, device=dev)
             ms = time_calls(lambda i: w8.linear_w8a8_block(xb, wsets[i][0], wsets[i][1], out=y, workspace=wsp), 4, R)
             out[f"decode_linear_block_m{M}"] = gemm_entry(ms, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
+            # the output quantised for the next layer: fused, and GEMM + quant_act_group
+            qo = (torch.empty(M, N, dtype=torch.int8, device=dev), torch.empty(M, N // 128, dtype=torch.float32, device=dev))
+            ms_f = time_calls(lambda i: w8.gemm_w8a8_block_quant(qa, sa, wsets[i][0], wsets[i][1], out=qo), 4, R)
+            ms_u = time_calls(lambda i: (w8.gemm_w8a8_block(qa, sa, wsets[i][0], wsets[i][1], out=y),
+                                         w8.quant_act_group(y, out=qo)), 4, R)
+            e = gemm_entry(ms_f, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
+            e["unfused_ms"] = round(ms_u, 4)
+            out[f"decode_fused_block_quant_m{M}"] = e
         del wsets
         torch.cuda.empty_cache()
 
@@ -412,6 +431,15 @@ def rows(args):
             out[f"gemm_block_grouped_{name}"] = {"ms": round(ms, 4), "TOPS": round(ops / ms / 1e9, 1),
                                                  "GBps": round(byts / ms / 1e6, 1),
                                                  "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+            if name == "moe_gate_up":
+                qo = (torch.empty(P, N, dtype=torch.int8, device=dev), torch.empty(P, N // 128, dtype=torch.float32,
+                                                                                 device=dev))
+                ms_f = time_calls(lambda i: w8.gemm_w8a8_block_grouped_quant(qa, sa, Wq, Ws, offs, out=qo), 1, 5, warm=1)
+                ms_u = time_calls(lambda i: (w8.gemm_w8a8_block_grouped(qa, sa, Wq, Ws, offs, out=y),
+                                             w8.quant_act_group(y, out=qo)), 1, 5, warm=1)
+                out["fused_grouped_quant_moe_gate_up"] = {"ms": round(ms_f, 4), "unfused_ms": round(ms_u, 4),
+                                                          "hbm_frac": round(byts / ms_f / 1e6 / PEAK_HBM_GBS, 3)}
+                del qo
             del Wq, Ws, qa, sa, y
             torch.cuda.empty_cache()
     return out

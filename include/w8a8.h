@@ -196,6 +196,30 @@ int gemm_w8a8_channel_noalloc(const int8_t* A, const float* a_scale,
                               int64_t K, void* stream);
 
 /*
+ * The block-wise GEMM with the quantiser of the next block-wise layer fused
+ * into its epilogue (page 1 section 2.3: activations are quantised online,
+ * per token-group, before every INT8 matmul; here the group quantisation of
+ * this GEMM's output runs where the output is produced instead of in a
+ * separate pass over it).  The result is exactly gemm_w8a8_block with bf16
+ * output followed by quant_act_group on that output:
+ *   y[m][n]       = bf16 of gemm_w8a8_block's fp32 value
+ *   q_scale[m][g] = fp32(max(amax over y[m][128 g .. 128 g + 127], 1e-10) / 127)
+ *   q[m][n]       = clamp(round_half_even(fp32(y[m][n] / q_scale[m][n/128])), -127, 127)
+ *   A, a_scale, W, w_scale as gemm_w8a8_block; N % 128 == 0 (W8_ERR_SHAPE
+ *   otherwise); q [M][N] int8 out, q_scale [M][N/128] fp32 out.
+ * The quantisation runs in the tile kernel's epilogue, or, for small tile
+ * grids, in the pass that sums the K slices (split-K workspace as for
+ * gemm_w8a8_block).  For decode-sized M (the weight-streaming kernels of
+ * gemm_w8a8_block, whose waves own 16-column slices of a group) the bf16
+ * output goes through the same per-stream scratch (M x N x 2 bytes) to the
+ * group quantiser: nothing is saved there, but the result is the same.
+ */
+int gemm_w8a8_block_quant(const int8_t* A, const float* a_scale,
+                          const int8_t* W, const float* w_scale,
+                          int8_t* q, float* q_scale,
+                          int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * The int32 block partial sums of the block-wise GEMM, for bit-exact checks:
  *   P [KB][M][N] int32, P[kb][m][n] as defined for gemm_w8a8_block.
  */
@@ -234,6 +258,19 @@ int gemm_w8a8_block_grouped(const int8_t* A, const float* a_scale,
                             const int32_t* expert_offsets, void* Y, int y_dtype,
                             int64_t E, int64_t P, int64_t N, int64_t K,
                             void* stream);
+
+/*
+ * gemm_w8a8_block_grouped with the next layer's group quantisation fused
+ * into its epilogue, as gemm_w8a8_block_quant: q [P][N] int8 and
+ * q_scale [P][N/128] fp32 out (rows in the same expert-sorted order),
+ * N % 128 == 0.
+ */
+int gemm_w8a8_block_grouped_quant(const int8_t* A, const float* a_scale,
+                                  const int8_t* W, const float* w_scale,
+                                  const int32_t* expert_offsets,
+                                  int8_t* q, float* q_scale,
+                                  int64_t E, int64_t P, int64_t N, int64_t K,
+                                  void* stream);
 
 /*
  * One-call linear layers (page 1 section 2.3: activations are quantised

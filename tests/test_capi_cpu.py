@@ -97,6 +97,16 @@ def test_gemm_argument_checks():
     assert L.gemm_w8a8_block_grouped(P16, P16, P16, P16, NUL, P16, w8.W8_BF16, 8, 4, 4, 128, NUL) == ENULL
     assert L.gemm_w8a8_block_grouped(P16, P16, P16, P16, P16, P16, w8.W8_I32, 8, 4, 4, 128, NUL) == EDTYPE
     assert L.gemm_w8a8_block_grouped(NUL, NUL, NUL, NUL, NUL, NUL, w8.W8_BF16, 8, 0, 4, 128, NUL) == OK
+    # fused output quantisation: N must be whole 128-column groups
+    assert L.gemm_w8a8_block_quant(P16, P16, P16, P16, P16, P16, 4, 100, 128, NUL) == ESHAPE
+    assert L.gemm_w8a8_block_quant(P16, P16, P16, P16, P16, P16, 4, 128, 100, NUL) == ESHAPE
+    assert L.gemm_w8a8_block_quant(P16, P16, P16, P16, P16, NUL, 4, 128, 128, NUL) == ENULL
+    assert L.gemm_w8a8_block_quant(P16, P16, P16, P16, P4, P16, 4, 128, 128, NUL) == EALIGN
+    assert L.gemm_w8a8_block_quant(NUL, NUL, NUL, NUL, NUL, NUL, 0, 128, 128, NUL) == OK
+    assert L.gemm_w8a8_block_grouped_quant(P16, P16, P16, P16, P16, P16, P16, 8, 4, 200, 128, NUL) == ESHAPE
+    assert L.gemm_w8a8_block_grouped_quant(P16, P16, P16, P16, P16, P16, P16, 5000, 4, 128, 128, NUL) == ESHAPE
+    assert L.gemm_w8a8_block_grouped_quant(P16, P16, P16, P16, NUL, P16, P16, 8, 4, 128, 128, NUL) == ENULL
+    assert L.gemm_w8a8_block_grouped_quant(NUL, NUL, NUL, NUL, NUL, NUL, NUL, 8, 0, 128, 128, NUL) == OK
 
 
 def test_linear_workspace_bytes():

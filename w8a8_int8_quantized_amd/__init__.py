@@ -52,6 +52,13 @@ _FUNCS = {
     "gemm_w8a8_channel_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "gemm_w8a8_block_quant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_void_p]),
+    "gemm_w8a8_block_grouped_quant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "gemm_w8a8_block_partials": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "gemm_w8a16_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -225,6 +232,33 @@ def gemm_w8a8_channel(A, a_scale, W, w_scale, out_dtype=torch.bfloat16, out=None
     _check(lib.gemm_w8a8_channel(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(y), _out_code(y.dtype), M, N, K,
                                  _stream()), "gemm_w8a8_channel")
     return y
+
+
+def gemm_w8a8_block_quant(A, a_scale, W, w_scale, out=None):
+    """Block-wise GEMM whose bf16 output is quantised per 1 x 128 group in the
+    epilogue (the next layer's activations): returns (q int8 [M, N], scales
+    fp32 [M, N/128]), equal to quant_act_group(gemm_w8a8_block(...))."""
+    _dev(A, W, a_scale, w_scale)
+    M, K = A.shape
+    N = W.shape[0]
+    q, s = out if out is not None else (_empty((M, N), torch.int8, A), _empty((M, N // GROUP), torch.float32, A))
+    _dev(q, s)
+    _check(lib.gemm_w8a8_block_quant(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(q), _p(s), M, N, K, _stream()),
+           "gemm_w8a8_block_quant")
+    return q, s
+
+
+def gemm_w8a8_block_grouped_quant(A, a_scale, W, w_scale, offsets, out=None):
+    """Grouped (MoE) block-wise GEMM with the output group quantisation fused:
+    returns (q int8 [P, N], scales fp32 [P, N/128])."""
+    _dev(A, W, a_scale, w_scale, offsets)
+    P, K = A.shape
+    E, N, _ = W.shape
+    q, s = out if out is not None else (_empty((P, N), torch.int8, A), _empty((P, N // GROUP), torch.float32, A))
+    _dev(q, s)
+    _check(lib.gemm_w8a8_block_grouped_quant(_p(A), _p(a_scale), _p(W), _p(w_scale), _p(offsets), _p(q), _p(s), E,
+                                             P, N, K, _stream()), "gemm_w8a8_block_grouped_quant")
+    return q, s
 
 
 def gemm_w8a8_channel_noalloc(A, a_scale, W, w_scale, out_dtype=torch.bfloat16, out=None):

@@ -186,6 +186,31 @@ int gemm_w8a8_channel_noalloc(const int8_t* A, const float* a_scale, const int8_
   return status_of(e);
 }
 
+int gemm_w8a8_block_quant(const int8_t* A, const float* a_scale, const int8_t* W, const float* w_scale, int8_t* q,
+                          float* q_scale, int64_t M, int64_t N, int64_t K, void* stream) {
+  int rc = check_gemm_common(A, W, q, M, N, K);
+  if (rc || M == 0 || N == 0) return rc;
+  if (K == 0 || (N & 127) != 0) return W8_ERR_SHAPE;
+  if (!a_scale || !w_scale || !q_scale) return W8_ERR_NULL;
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(q_scale, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_gemm_block_q8(A, a_scale, W, w_scale, q, q_scale, M, N, K, as_stream(stream)));
+}
+
+int gemm_w8a8_block_grouped_quant(const int8_t* A, const float* a_scale, const int8_t* W, const float* w_scale,
+                                  const int32_t* expert_offsets, int8_t* q, float* q_scale, int64_t E, int64_t P,
+                                  int64_t N, int64_t K, void* stream) {
+  if (E < 0 || E > 4096) return W8_ERR_SHAPE;
+  int rc = check_gemm_common(A, W, q, P, N, K);
+  if (rc || P == 0 || N == 0 || E == 0) return rc;
+  if (K == 0 || (N & 127) != 0) return W8_ERR_SHAPE;
+  if (N * K > kMaxElems / E) return W8_ERR_SHAPE;
+  if (!a_scale || !w_scale || !expert_offsets || !q_scale) return W8_ERR_NULL;
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(expert_offsets, 4) || !aligned(q_scale, 4))
+    return W8_ERR_ALIGN;
+  return status_of(w8::launch_gemm_block_grouped_q8(A, a_scale, W, w_scale, expert_offsets, q, q_scale, E, P, N, K,
+                                                    as_stream(stream)));
+}
+
 int gemm_w8a8_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
                              void* stream) {
   int rc = check_gemm_common(A, W, P, M, N, K);

@@ -43,7 +43,8 @@ template <int MODE, int OUT, int NWM>
 __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                              const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                              const int32_t* __restrict__ offsets, void* __restrict__ Y,
-                                                             int M, int N, int K, int TM, int TN, int E) {
+                                                             int M, int N, int K, int TM, int TN, int E,
+                                                             float* __restrict__ qs = nullptr) {
   constexpr int BM = 64 * NWM, BN = 256, NWV = 2 * NWM;
   constexpr int STG = (BM + BN) * 128;
   constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A (= 4)
@@ -69,8 +70,10 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     Wx = W + (int64_t)g.e * N * K;
     swx = sw + (int64_t)g.e * NB * KB;
   } else {
+    // strips of up to 8 row tiles per XCD band: an XCD's concurrent tiles
+    // share both operands' panels in its L2 (tile_common.h)
     int tm, tn;
-    xcd_tile(blockIdx.x, TM, TN, tm, tn);
+    strip_tile(blockIdx.x, TM, TN, TM < 8 ? TM : 8, tm, tn);
     m0 = tm * BM;
     n0 = tn * BN;
     mrows = M - m0 < BM ? M - m0 : BM;
@@ -228,6 +231,46 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   waitcnt<0, 0>();
   if (!DQ) return;
 
+  if (OUT == OUT_Q8) {
+    // The 128 columns of this wave are one quantisation group of the next
+    // layer (1 x 128 along its K = this N), and a row's 128 values sit in two
+    // lanes (l and l ^ 32, 64 each): round to bf16, take the group's amax
+    // over the pair, quantise as quant_act_group does, and store 4 codes per
+    // 4-byte write; lanes 0..31 store the row's scale.  The caller
+    // guarantees N % 128 == 0, so a group is never ragged.
+    if (!wact || n0 + wn * 128 >= N) return;
+    const int G = N >> 7;
+    const int grp = (n0 + wn * 128) >> 7;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            facc[i][j][g][r] = bf16_lo(f32_to_bf16_rne(facc[i][j][g][r]));
+            a = fmaxf(a, __builtin_fabsf(facc[i][j][g][r]));
+          }
+      a = fmaxf(a, __shfl_xor(a, 32));
+      const QScale sc = make_scale(a);
+      const int ml = wm * 64 + j * 32 + (lane & 31);
+      if (ml >= mrows) continue;
+      const int64_t m = m0 + ml;
+      int8_t* qrow = static_cast<int8_t*>(Y) + m * N + n0 + wn * 128 + 4 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const v4f v = facc[i][j][g];
+          *reinterpret_cast<uint32_t*>(qrow + i * 32 + g * 8) =
+              pack4(quant_one(v[0], sc), quant_one(v[1], sc), quant_one(v[2], sc), quant_one(v[3], sc));
+        }
+      if (lane < 32) qs[m * G + grp] = sc.s;
+    }
+    return;
+  }
   if (OUT == OUT_BF16) {
     // the bf16 tile goes through LDS (row r of 256 bf16, 16-byte chunk c at
     // c ^ (r & 15)) so that it leaves in whole rows; the barrier also means
@@ -261,7 +304,8 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
       if (r >= mrows || n >= N) continue;
       uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)(m0 + r) * N + n;
       if (vec8) {
-        *reinterpret_cast<v4i*>(y) = v;
+        // written once, not read back by this kernel
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(y));
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -289,9 +333,10 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
 
 template <int MODE, int OUT, int NWM>
 void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float* sa, const int8_t* W,
-                         const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E) {
+                         const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E,
+                         float* qs = nullptr) {
   hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM>), grid, dim3(128 * NWM), 0, st, A, sa, W, sw, off, Y, M, N, K, TM,
-                     TN, E);
+                     TN, E, qs);
 }
 
 // Sum of the S fp32 slices' partial tiles, in slice order, then the output.
@@ -311,6 +356,38 @@ __global__ __launch_bounds__(256) void k_splitk_sum_f32(const float* __restrict_
     for (int r = 0; r < 4; ++r)
       if (n + r < N) o[r] = __fadd_rn(o[r], ws[sl * MN + idx + r]);
   store4<OUT>(Y, idx, n, N, (N & 3) == 0, o[0], o[1], o[2], o[3]);
+}
+
+// The same sum in slice order, rounded to bf16 and quantised per 1 x 128
+// group along N as quant_act_group does: a group is 32 consecutive threads
+// (N % 128 == 0 keeps it inside one row and one half of a wave).
+__global__ __launch_bounds__(256) void k_splitk_sum_f32_q8(const float* __restrict__ ws, int S, int M, int N,
+                                                           int8_t* __restrict__ q, float* __restrict__ qs) {
+  const int64_t q4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nq = N >> 2;
+  const bool live = q4 < (int64_t)M * nq;
+  const int m = live ? (int)(q4 / nq) : 0, n = live ? (int)(q4 - (int64_t)m * nq) * 4 : 0;
+  const int64_t idx = (int64_t)m * N + n;
+  const int64_t MN = (int64_t)M * N;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live)
+    for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = __fadd_rn(o[r], ws[sl * MN + idx + r]);
+  float a = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    o[r] = bf16_lo(f32_to_bf16_rne(o[r]));
+    a = fmaxf(a, __builtin_fabsf(o[r]));
+  }
+  // max over the 32 lanes of this half-wave (the group)
+  a = max16(a);
+  a = fmaxf(a, __shfl_xor(a, 16));
+  const QScale sc = make_scale(a);
+  if (!live) return;
+  *reinterpret_cast<uint32_t*>(q + idx) =
+      pack4(quant_one(o[0], sc), quant_one(o[1], sc), quant_one(o[2], sc), quant_one(o[3], sc));
+  if ((threadIdx.x & 31) == 0) qs[(int64_t)m * (N >> 7) + (n >> 7)] = sc.s;
 }
 
 }  // namespace
@@ -357,6 +434,67 @@ hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, 
     else
       hipLaunchKernelGGL((k_splitk_sum_f32<OUT_F32>), rg, dim3(256), 0, st, wsf, S, (int)M, (int)N, Y);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_block_q8(const int8_t* A, const float* sa, const int8_t* W, const float* sw, int8_t* q,
+                                float* qs, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (decode_path_takes(M, N, false)) {
+    // decode-sized M: the weight-streaming kernel that gemm_w8a8_block runs
+    // (a wave owns 16 columns, a group spans 8 waves), its bf16 output in the
+    // stream's scratch, then the group quantiser; the lease is held until
+    // both are enqueued
+    const WsLease lease = stream_workspace(st, 0, (size_t)M * N * 2);
+    if (lease.status() != kWsOk) return ws_error(lease);
+    const hipError_t e = launch_gemm_block_decode(A, sa, W, sw, lease.ptr(), OUT_BF16, M, N, K, st);
+    if (e != hipSuccess) return e;
+    return launch_quant_group(lease.ptr(), false, M, N, q, qs, st);
+  }
+  // the tile kernels, tile height and K split as in launch_gemm_block (the
+  // same kernels, so the same fp32 sums and bf16 values)
+  const int TN = (int)((N + 255) / 256);
+  const int BM = (M <= 128 || ((M + 255) / 256) * TN < kTileCUs) ? 128 : 256;
+  const int TM = (int)((M + BM - 1) / BM);
+  const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, BM == 256 ? 2.6 : 1.7);
+  const dim3 grid((unsigned)(TM * TN), (unsigned)S);
+  if (S == 1) {
+    if (BM == 128)
+      launch_block_kernel<MODE_DEQUANT, OUT_Q8, 2>(grid, st, A, sa, W, sw, nullptr, q, (int)M, (int)N, (int)K, TM, TN,
+                                                   0, qs);
+    else
+      launch_block_kernel<MODE_DEQUANT, OUT_Q8, 4>(grid, st, A, sa, W, sw, nullptr, q, (int)M, (int)N, (int)K, TM, TN,
+                                                   0, qs);
+    return hipGetLastError();
+  }
+  // fp32 slices in the stream's scratch, held until the reduction is enqueued
+  const WsLease lease = stream_workspace(st, 0, (size_t)S * M * N * 4);
+  if (lease.status() != kWsOk) return ws_error(lease);
+  if (BM == 128)
+    launch_block_kernel<MODE_DEQUANT, OUT_F32, 2>(grid, st, A, sa, W, sw, nullptr, lease.ptr(), (int)M, (int)N, (int)K,
+                                                  TM, TN, 0);
+  else
+    launch_block_kernel<MODE_DEQUANT, OUT_F32, 4>(grid, st, A, sa, W, sw, nullptr, lease.ptr(), (int)M, (int)N, (int)K,
+                                                  TM, TN, 0);
+  const dim3 rg((unsigned)((M * (N / 4) + 255) / 256));
+  hipLaunchKernelGGL(k_splitk_sum_f32_q8, rg, dim3(256), 0, st, static_cast<const float*>(lease.ptr()), S, (int)M,
+                     (int)N, q, qs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_block_grouped_q8(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
+                                        const int32_t* offsets, int8_t* q, float* qs, int64_t E, int64_t P,
+                                        int64_t N, int64_t K, hipStream_t st) {
+  const int TN = (int)((N + 255) / 256);
+  const bool big = P >= 96 * E;
+  const int BM = big ? 256 : 128;
+  const int64_t TMmax = (P + BM - 1) / BM + E;
+  const dim3 grid((unsigned)(TMmax * TN));
+  if (big)
+    launch_block_kernel<MODE_GROUPED, OUT_Q8, 4>(grid, st, A, sa, W, sw, offsets, q, (int)P, (int)N, (int)K,
+                                                 (int)TMmax, TN, (int)E, qs);
+  else
+    launch_block_kernel<MODE_GROUPED, OUT_Q8, 2>(grid, st, A, sa, W, sw, offsets, q, (int)P, (int)N, (int)K,
+                                                 (int)TMmax, TN, (int)E, qs);
   return hipGetLastError();
 }
 

@@ -10,7 +10,9 @@
 
 namespace w8 {
 
-enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_I32 = 2 };
+// OUT_Q8: the bf16 output quantised per 1 x 128 group along N (the next
+// block-wise layer's activations): int8 codes in Y, fp32 scales [M][N/128].
+enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_I32 = 2, OUT_Q8 = 3 };
 
 hipError_t launch_quant_group(const void* x, bool fp16, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st);
 hipError_t launch_quant_token(const void* x, bool fp16, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t st);
@@ -29,6 +31,14 @@ hipError_t launch_gemm_channel_noalloc(const int8_t* A, const float* sa, const i
                                        OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st, bool* too_big);
 hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                              OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st);
+// The block-wise GEMM with its bf16 output quantised per token-group in the
+// epilogue: codes q [M][N] and scales qs [M][N/128] (N % 128 == 0), equal to
+// gemm_w8a8_block's bf16 output passed through quant_act_group.
+hipError_t launch_gemm_block_q8(const int8_t* A, const float* sa, const int8_t* W, const float* sw, int8_t* q,
+                                float* qs, int64_t M, int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_gemm_block_grouped_q8(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
+                                        const int32_t* offsets, int8_t* q, float* qs, int64_t E, int64_t P,
+                                        int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
                                       hipStream_t st);
 hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int8_t* W, const float* sw,

@@ -50,22 +50,13 @@ __device__ __forceinline__ void store4i(int32_t* y, int n, int N, bool vec, v4i 
 }
 
 // Workgroup -> tile.  The hardware dispatches workgroup b to XCD b % 8, and
-// each XCD has its own L2.  Tiles t = x*T/8 .. (x+1)*T/8 - 1 (M fastest) go
-// to XCD x, so an XCD owns a contiguous band of N tiles: every W panel is
-// pulled into one L2 only, and the XCD's concurrent workgroups share it.
-__device__ __forceinline__ void xcd_tile(int b, int TM, int TN, int& tm, int& tn) {
-  const int T = TM * TN;
-  const int x = b & 7, j = b >> 3;
-  const int T8 = T >> 3, rem = T & 7;
-  const int t = x * T8 + (x < rem ? x : rem) + j;
-  tm = t % TM;
-  tn = t / TM;
-}
-
-// The same band of the tile sequence per XCD, with the sequence walking
-// strips of GM row tiles (m fastest inside a strip): an XCD's 32 concurrent
-// workgroups then cover about GM row tiles x 32 / GM column tiles and share
-// both operands' panels in its L2.  GM = TM is xcd_tile's order.
+// each XCD has its own L2.  Tiles t = x*T/8 .. (x+1)*T/8 - 1 of the sequence
+// go to XCD x (a contiguous band), and the sequence walks strips of GM row
+// tiles (m fastest inside a strip): an XCD's 32 concurrent workgroups then
+// cover about GM row tiles x 32 / GM column tiles and share both operands'
+// panels in its L2 (with GM = TM, one column of row tiles at a time, an
+// XCD's 32 workgroups span 2 column tiles x 16 row tiles at M = 4096 and
+// fetch each K block's panels once per 18 tiles instead of once per 12).
 __device__ __forceinline__ void strip_tile(int b, int TM, int TN, int GM, int& tm, int& tn) {
   const int T = TM * TN;
   const int x = b & 7, j = b >> 3;
