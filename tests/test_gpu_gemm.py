@@ -388,6 +388,21 @@ def test_channel_up_to_128_rows_wide(M, N):
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
 
 
+# Up to 128 rows where N does not balance the decode kernel: the tile kernel
+# split over K with the upper half of its row tile idle (waves 4..7 only
+# load), int32 slice sums, ragged N and one-block slices (K = 2048, 16 slices).
+@pytest.mark.parametrize("M,N,K", [(72, 1000, 4096), (128, 2000, 2048), (100, 520, 2048)])
+def test_channel_split_k_up_to_128_rows(M, N, K):
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M + N + 11, scheme="channel")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    ACC, y64, y32 = gemm.gemm_channel(qa, sa, qw, sw)
+    assert np.array_equal(_np(w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.int32)), ACC)
+    yf = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.float32)
+    assert np.array_equal(_np(yf).view(np.uint32), y32.view(np.uint32))
+    yb = w8.gemm_w8a8_channel(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+
+
 def test_gemms_are_deterministic():
     qa, sa, qw, sw = _inputs(300, 576, 1024, seed=2, scheme="block")
     A, SA, W, SW = _dev(qa, sa, qw, sw)

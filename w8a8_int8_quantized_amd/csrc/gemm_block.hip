@@ -351,10 +351,20 @@ __global__ __launch_bounds__(256) void k_splitk_sum_f32(const float* __restrict_
   const int64_t idx = (int64_t)m * N + n;
   const int64_t MN = (int64_t)M * N;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int sl = 0; sl < S; ++sl)
+  if ((N & 3) == 0) {
+    // 16-byte loads, four slices in flight; the sum stays in slice order
+#pragma unroll 4
+    for (int sl = 0; sl < S; ++sl) {
+      const v4f v = *reinterpret_cast<const v4f*>(ws + sl * MN + idx);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n + r < N) o[r] = __fadd_rn(o[r], ws[sl * MN + idx + r]);
+      for (int r = 0; r < 4; ++r) o[r] = __fadd_rn(o[r], v[r]);
+    }
+  } else {
+    for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) o[r] = __fadd_rn(o[r], ws[sl * MN + idx + r]);
+  }
   store4<OUT>(Y, idx, n, N, (N & 3) == 0, o[0], o[1], o[2], o[3]);
 }
 
@@ -371,9 +381,12 @@ __global__ __launch_bounds__(256) void k_splitk_sum_f32_q8(const float* __restri
   const int64_t MN = (int64_t)M * N;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   if (live)
-    for (int sl = 0; sl < S; ++sl)
+#pragma unroll 4
+    for (int sl = 0; sl < S; ++sl) {
+      const v4f v = *reinterpret_cast<const v4f*>(ws + sl * MN + idx);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = __fadd_rn(o[r], ws[sl * MN + idx + r]);
+      for (int r = 0; r < 4; ++r) o[r] = __fadd_rn(o[r], v[r]);
+    }
   float a = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {

@@ -55,7 +55,12 @@ constexpr unsigned kChOob = 0x20000000u;   // added to a load's offset: past eve
 // q - 128, prm = {s, z}, wsum = per-row weight sums) in place of the
 // channel-wise one: Y = fp32(fp32(s * sw[n]) * fp32(fp32(ACC + 128 WS[n]) -
 // fp32(z * fp32(WS[n])))).
-template <int OUT, int FN, bool AS = false>
+// HALF (int32 output, M <= 128): tile rows 128..255 lie past M, so waves 4..7
+// (whose 64-row bands those are) issue only their share of the stage loads
+// and meet the barriers; their SIMDs then run one MFMA wave each and the
+// tile's MFMA work halves (a decode-sized M split over K is otherwise bound
+// by multiplying rows that are never stored).
+template <int OUT, int FN, bool AS = false, bool HALF = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                          void* __restrict__ Y, int M, int N, int K, int TM, int GM,
@@ -138,6 +143,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restric
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                 \
       acc[g][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(WC[g], AC[j], acc[g][j], 0, 0, 0);        \
     __builtin_amdgcn_sched_barrier(0);                                                            \
+  }
+
+  if (HALF && wave >= 4) {
+    // the same loads and barriers as the MFMA waves below, nothing else;
+    // their rows are never stored (int32 output only)
+    static_assert(!HALF || (OUT == OUT_I32 && !AS), "HALF: int32 output only");
+#pragma unroll
+    for (int d = 0; d < 8; ++d) CH_LOAD(0, d, 0u)
+    wait_barrier<0, 15>();
+    {
+      const unsigned so1 = 1 < NK ? 0u : kChOob;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) CH_LOAD(1, d, so1)
+    }
+    for (int kb = 0; kb + 1 < NK; ++kb) {
+      wait_barrier<0, 0>();
+      const unsigned so = kb + 2 < NK ? 0u : kChOob;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) CH_LOAD(kb + 2, d, so)
+    }
+    waitcnt<0, 0>();
+    return;
   }
 
   // prologue: block 0 loaded and visible, block 1 in flight
@@ -301,12 +328,18 @@ __global__ __launch_bounds__(256) void k_splitk_sum_i32(const int32_t* __restric
   const int m = (int)(q4 / nq), n = (int)(q4 - (int64_t)m * nq) * 4;
   const int64_t idx = (int64_t)m * N + n;
   const int64_t MN = (int64_t)M * N;
-  v4i a = {0, 0, 0, 0};
-  for (int sl = 0; sl < S; ++sl)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n + r < N) a[r] += ws[sl * MN + idx + r];
   const bool vec = (N & 3) == 0;
+  v4i a = {0, 0, 0, 0};
+  if (vec) {
+    // 16-byte loads, four slices in flight
+#pragma unroll 4
+    for (int sl = 0; sl < S; ++sl) a += *reinterpret_cast<const v4i*>(ws + sl * MN + idx);
+  } else {
+    for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) a[r] += ws[sl * MN + idx + r];
+  }
   if (OUT == OUT_I32) {
     store4i(static_cast<int32_t*>(Y) + idx, n, N, vec, a);
   } else {
@@ -474,8 +507,13 @@ int channel_slices(int64_t M, int64_t N, int64_t K) {
 hipError_t channel_split(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, OutKind out,
                          int64_t M, int64_t N, int64_t K, int S, void* ws, hipStream_t st) {
   const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + 255) / 256);
-  hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), dim3((unsigned)(TM * TN), (unsigned)S), dim3(512), 0, st, A, sa,
-                     W, sw, ws, (int)M, (int)N, (int)K, TM, channel_strip(TM));
+  const dim3 grid((unsigned)(TM * TN), (unsigned)S);
+  if (M <= 128)
+    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8, false, true>), grid, dim3(512), 0, st, A, sa, W, sw, ws, (int)M,
+                       (int)N, (int)K, TM, channel_strip(TM));
+  else
+    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), grid, dim3(512), 0, st, A, sa, W, sw, ws, (int)M, (int)N, (int)K,
+                       TM, channel_strip(TM));
   const dim3 rg((unsigned)((M * ((N + 3) / 4) + 255) / 256));
   const int32_t* wsi = static_cast<const int32_t*>(ws);
   switch (out) {
