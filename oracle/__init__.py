@@ -32,6 +32,8 @@ Modules:
              FP8 -> BF16 -> INT8 requantisation
   gemm     - block-wise, channel-wise, W8A16 group-wise and grouped MoE GEMMs
   routing  - top-k expert routing used to lay out the grouped GEMM inputs
+  asym     - the asymmetric uint8 activation variant
+  int4     - group-wise INT4 weights (packed two per byte) and the W4A16 GEMM
 """
 
-from . import formats, quant, gemm, routing  # noqa: F401
+from . import formats, quant, gemm, routing, int4  # noqa: F401
