@@ -400,6 +400,25 @@ def rows(args):
                                                     "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
             del ws_
         torch.cuda.empty_cache()
+        # --- decode W4A16: the same linears with INT4 group-wise weights
+        # (packed two per byte), 40 weight copies (> 1 GB)
+        for name in ("w8a16_qkv", "w8a16_down"):
+            K, N = synth.SHAPES[name]
+            ws_ = []
+            for s in range(40):
+                w = synth.weights(N, K, seed=40 + s, device=dev, dtype=torch.float16)
+                ws_.append(w8.quant_weight_int4_group(w))
+                del w
+            for M in (1, 8, 32, 64):
+                xx = synth.activations(M, K, seed=M, device=dev, dtype=torch.float16)
+                y = torch.empty(M, N, dtype=torch.float16, device=dev)
+                ms = time_calls(lambda i: w8.gemm_w4a16_group(xx, ws_[i][0], ws_[i][1], out=y), 40, R)
+                byts = N * K // 2 + 4 * N * (K // 128) + 2 * M * K + 2 * M * N
+                short = name.replace("w8a16_", "")
+                out[f"decode_w4a16_{short}_m{M}"] = {"ms": round(ms, 4), "GBps": round(byts / ms / 1e6, 1),
+                                                     "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+            del ws_
+        torch.cuda.empty_cache()
 
     if want("moe"):
         # --- MoE: 256 experts, top-8 of 4096 tokens

@@ -14,8 +14,8 @@
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  Calls
  *     are thread-safe.  The only state the library keeps is its own scratch
  *     (described at gemm_w8a8_block): a split-K workspace per (device,
- *     stream) for gemm_w8a8_block, gemm_w8a8_channel, gemm_w8a16_group and
- *     the linear_* calls, one for quant_act_asym and gemm_w8a8_asym, and the
+ *     stream) for gemm_w8a8_block, gemm_w8a8_channel, gemm_w8a16_group,
+ *     gemm_w4a16_group and the linear_* calls, one for quant_act_asym and gemm_w8a8_asym, and the
  *     fixed array of gemm_w8a8_channel_noalloc; every other entry point
  *     allocates nothing.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
@@ -27,7 +27,8 @@
  *     NB = ceil(N / 128).  M == 0 (or N == 0) is a valid no-op.
  *   - Data pointers (int8, bf16, fp16, fp8, outputs) must be 16-byte aligned;
  *     scale pointers 4-byte aligned.  Outputs must not alias inputs.
- *   - int8 codes are always in [-127, 127]; scales are fp32.
+ *   - int8 codes are always in [-127, 127] (INT4 codes in [-7, 7]); scales
+ *     are fp32.
  *   - bf16 and fp16 values are passed as their 16-bit patterns.
  *   - Inputs are finite.  NaN or infinite inputs (and the FP8 NaN codes
  *     0x7F / 0xFF) give unspecified results but never out-of-bounds access.
@@ -239,6 +240,33 @@ int gemm_w8a8_block_partials(const int8_t* A, const int8_t* W, int32_t* P,
  * deterministic, with the fp32 rounding of that order.
  */
 int gemm_w8a16_group(const uint16_t* x, const int8_t* W, const float* w_scale,
+                     uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * INT4 group-wise weight quantisation.  Page 3 ("DeepSeek-R1-Distill-Llama-8B
+ * quantisation practice", section 3.3) reports INT4 against INT8 by
+ * measurement only; the scheme here is the group-wise weight scheme of the
+ * W8A16 variant (page 5) with a 4-bit range: per row of W and group of 128
+ * along K, s = fp32(max(amax, 1e-10) / 7) and q = clamp(rne(fp32(w / s)),
+ * -7, 7) (-8 unused).  Codes are stored two per byte in offset binary:
+ * byte j of a row holds q[2j] + 8 in its low nibble and q[2j+1] + 8 in its
+ * high nibble.
+ *   w       [N][K]   bf16 (w_dtype = W8_BF16) or fp16 (W8_FP16)
+ *   w4      [N][K/2] uint8 out (16-byte aligned)
+ *   w_scale [N][KB]  fp32 out
+ */
+int quant_weight_int4_group(const void* w, int w_dtype, int64_t N, int64_t K,
+                            uint8_t* w4, float* w_scale, void* stream);
+
+/*
+ * W4A16 group-wise GEMM: gemm_w8a16_group's formula, with every code read
+ * from the INT4 layout of quant_weight_int4_group (nibble value minus 8):
+ *   Y[m][n] = sum_g w_scale[n][g] * sum_{k in group g} x[m][k] * q[n][k]
+ *   x [M][K] fp16, W4 [N][K/2] uint8, w_scale [N][KB] fp32, Y [M][N] fp16.
+ * Products are exact in fp32 and sums fp32; the kernels, the K split and its
+ * workspace are those of gemm_w8a16_group, so the same rules apply.
+ */
+int gemm_w4a16_group(const uint16_t* x, const uint8_t* W4, const float* w_scale,
                      uint16_t* Y, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*

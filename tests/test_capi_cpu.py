@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert w8.lib.w8_abi_version() == 2
+    assert w8.lib.w8_abi_version() == 3
     for rc in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, -5, EWS, ECAP):
         assert len(w8.lib.w8_status_string(rc)) > 0
     assert w8.lib.w8_status_string(99) == b"unknown status"
@@ -107,6 +107,25 @@ def test_gemm_argument_checks():
     assert L.gemm_w8a8_block_grouped_quant(P16, P16, P16, P16, P16, P16, P16, 5000, 4, 128, 128, NUL) == ESHAPE
     assert L.gemm_w8a8_block_grouped_quant(P16, P16, P16, P16, NUL, P16, P16, 8, 4, 128, 128, NUL) == ENULL
     assert L.gemm_w8a8_block_grouped_quant(NUL, NUL, NUL, NUL, NUL, NUL, NUL, 8, 0, 128, 128, NUL) == OK
+
+
+def test_int4_argument_checks():
+    L = w8.lib
+    fn = L.quant_weight_int4_group
+    assert fn(P16, 0, 4, 100, P16, P16, NUL) == ESHAPE          # K % 128 != 0
+    assert fn(P16, 0, -1, 128, P16, P16, NUL) == ESHAPE
+    assert fn(P16, w8.W8_FP32, 4, 128, P16, P16, NUL) == EDTYPE
+    assert fn(NUL, 0, 4, 128, P16, P16, NUL) == ENULL
+    assert fn(P16, 0, 4, 128, NUL, P16, NUL) == ENULL
+    assert fn(P16, 0, 4, 128, P4, P16, NUL) == EALIGN
+    assert fn(P16, 0, 0, 128, NUL, NUL, NUL) == OK              # N == 0: no-op
+    g = L.gemm_w4a16_group
+    assert g(P16, P16, P16, P16, 4, 4, 96, NUL) == ESHAPE
+    assert g(P16, P16, P16, P16, 4, 4, 0, NUL) == ESHAPE
+    assert g(P16, P4, P16, P16, 4, 4, 128, NUL) == EALIGN
+    assert g(P16, P16, P4, P4, 4, 4, 128, NUL) == EALIGN
+    assert g(P16, NUL, P16, P16, 4, 4, 128, NUL) == ENULL
+    assert g(NUL, NUL, NUL, NUL, 0, 4, 128, NUL) == OK
 
 
 def test_linear_workspace_bytes():

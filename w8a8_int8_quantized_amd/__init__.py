@@ -63,6 +63,10 @@ _FUNCS = {
                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "gemm_w8a16_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "quant_weight_int4_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "gemm_w4a16_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "gemm_w8a8_block_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -293,6 +297,34 @@ def gemm_w8a16_group(x, W, w_scale, out=None):
     N = W.shape[0]
     y = out if out is not None else _empty((M, N), torch.float16, x)
     _check(lib.gemm_w8a16_group(_p(x), _p(W), _p(w_scale), _p(y), M, N, K, _stream()), "gemm_w8a16_group")
+    return y
+
+
+def quant_weight_int4_group(w, out=None):
+    """Group-wise (1x128) INT4 quantisation of weights w [N, K] (bf16 or fp16):
+    packed codes uint8 [N, K/2] (two offset-binary nibbles per byte) and
+    scales fp32 [N, K/128]."""
+    _dev(w)
+    N, K = w.shape
+    q, s = out if out is not None else (_empty((N, K // 2), torch.uint8, w), _empty((N, K // GROUP), torch.float32, w))
+    _check(lib.quant_weight_int4_group(_p(w), _act_dtype(w), N, K, _p(q), _p(s), _stream()),
+           "quant_weight_int4_group")
+    return q, s
+
+
+def gemm_w4a16_group(x, W4, w_scale, out=None):
+    """W4A16: fp16 x [M, K], packed INT4 W4 [N, K/2], group scales [N, K/128] -> fp16 Y [M, N]."""
+    _dev(x, W4, w_scale)
+    if x.dtype != torch.float16:
+        raise W8Error("gemm_w4a16_group takes fp16 activations")
+    if W4.dtype != torch.uint8:
+        raise W8Error("gemm_w4a16_group takes packed uint8 weights")
+    M, K = x.shape
+    N = W4.shape[0]
+    if W4.shape[1] * 2 != K:
+        raise W8Error("gemm_w4a16_group: W4 must be [N, K/2]")
+    y = out if out is not None else _empty((M, N), torch.float16, x)
+    _check(lib.gemm_w4a16_group(_p(x), _p(W4), _p(w_scale), _p(y), M, N, K, _stream()), "gemm_w4a16_group")
     return y
 
 

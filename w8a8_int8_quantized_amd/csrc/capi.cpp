@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
@@ -230,6 +230,31 @@ int gemm_w8a16_group(const uint16_t* x, const int8_t* W, const float* w_scale, u
   if (!x || !W || !w_scale || !Y) return W8_ERR_NULL;
   if (!aligned(x, 16) || !aligned(W, 16) || !aligned(Y, 16) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
   return status_of(w8::launch_gemm_w8a16(x, W, w_scale, Y, M, N, K, as_stream(stream)));
+}
+
+int quant_weight_int4_group(const void* w, int w_dtype, int64_t N, int64_t K, uint8_t* w4, float* w_scale,
+                            void* stream) {
+  if (w_dtype != W8_BF16 && w_dtype != W8_FP16) return W8_ERR_DTYPE;
+  int rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (N == 0 || K == 0) return W8_OK;
+  if (!w || !w4 || !w_scale) return W8_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(w4, 16) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_quant_weight_int4(w, w_dtype == W8_FP16, N, K, w4, w_scale, as_stream(stream)));
+}
+
+int gemm_w4a16_group(const uint16_t* x, const uint8_t* W4, const float* w_scale, uint16_t* Y, int64_t M, int64_t N,
+                     int64_t K, void* stream) {
+  int rc = check_rows_k(M, K);
+  if (rc) return rc;
+  rc = check_rows_k(N, K);
+  if (rc) return rc;
+  if (M > 0 && N > 0 && M > kMaxElems / N) return W8_ERR_SHAPE;
+  if (M == 0 || N == 0) return W8_OK;
+  if (K == 0) return W8_ERR_SHAPE;
+  if (!x || !W4 || !w_scale || !Y) return W8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(W4, 16) || !aligned(Y, 16) || !aligned(w_scale, 4)) return W8_ERR_ALIGN;
+  return status_of(w8::launch_gemm_w4a16(x, W4, w_scale, Y, M, N, K, as_stream(stream)));
 }
 
 int gemm_w8a8_block_grouped(const int8_t* A, const float* a_scale, const int8_t* W, const float* w_scale,

@@ -76,6 +76,16 @@ __device__ __forceinline__ QScale make_scale(float amax) {
   return q;
 }
 
+// The group scale of the INT4 weight quantiser (the same quantiser with a
+// 4-bit range): fp32(max(amax, eps) / 7).  quant_one's estimate-and-guard
+// argument holds a fortiori for |x / s| <= 7.
+__device__ __forceinline__ QScale make_scale4(float amax) {
+  QScale q;
+  q.s = fmaxf(amax, kEps) / 7.0f;      // correctly rounded fp32 division
+  q.r = 1.0f / q.s;
+  return q;
+}
+
 // rne(fp32(x / s)) as a float holding an integer in [-127, 127].
 __device__ __forceinline__ float quant_one(float x, QScale sc) {
   float y = __fmul_rn(x, sc.r);

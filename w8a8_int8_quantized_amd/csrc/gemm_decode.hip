@@ -16,6 +16,8 @@
 //   (Meituan), section 2.3 (per-K-block dequant vs one epilogue dequant);
 //   W8A16 group-wise: "DeepSeek-R1-0528-Qwen3-8B Int8 W8A16" release note
 //   (symmetric group-wise INT8 weights, fp16 activations).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "pipeline.h"
@@ -24,6 +26,7 @@ namespace w8 {
 namespace {
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // SIMDs per GPU the dispatchers size grids against (256 CUs x 4).
 constexpr int kSimds = 256 * 4;
@@ -81,6 +84,9 @@ __device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
 }
 __device__ __forceinline__ v4i bl16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ v2i bl8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 __device__ __forceinline__ float blf(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
@@ -479,6 +485,60 @@ __device__ __forceinline__ v8h i8x8_to_f16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// INT4 weights: a 32-bit word holds the codes of 8 consecutive k as
+// offset-binary nibbles u = q + 8 (the even k in the low nibble of its byte).
+// The nibbles are spread one per byte in k order, then each byte u goes under
+// the high byte 0x64 (the fp16 value 1024 + u) and 1032 is subtracted: q
+// exactly.
+__device__ __forceinline__ v8h i4x8_to_f16(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;           // k = 0, 2, 4, 6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;    // k = 1, 3, 5, 7
+  const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // k = 0 .. 3
+  const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // k = 4 .. 7
+  uint32_t h2[4];
+  h2[0] = __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u);
+  h2[1] = __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u);
+  h2[2] = __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u);
+  h2[3] = __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u);
+  v8h r;
+  const v2h bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2h h = __builtin_bit_cast(v2h, h2[i]) - bias;
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
+// The weight registers of one 128-wide group for one lane: 32 int8 codes
+// (two 16-byte loads) or 32 INT4 codes (two 8-byte loads), k = 64 h + 16 q +
+// [0, 16) for h = 0, 1; and their fp16 values, 8 per MFMA operand.
+template <bool W4>
+struct WFrag {
+  using T = typename std::conditional<W4, v2i, v4i>::type;
+  static constexpr int kBytesPerGroup = W4 ? 64 : 128;   // bytes of one row per 128-wide group
+  static constexpr int kLaneBytes = W4 ? 8 : 16;         // bytes of a lane's 16 consecutive k
+  __device__ static T load(rsrc_t r, uint32_t off) {
+    if constexpr (W4) return bl8(r, off);
+    else return bl16(r, off);
+  }
+  // wh[t]: k = 64 (t / 2) + 16 q + 8 (t % 2) + [0, 8)
+  __device__ static void to_f16(const T& w0, const T& w1, v8h (&wh)[4]) {
+    if constexpr (W4) {
+      wh[0] = i4x8_to_f16((uint32_t)w0[0]);
+      wh[1] = i4x8_to_f16((uint32_t)w0[1]);
+      wh[2] = i4x8_to_f16((uint32_t)w1[0]);
+      wh[3] = i4x8_to_f16((uint32_t)w1[1]);
+    } else {
+      wh[0] = i8x8_to_f16(w0[0], w0[1]);
+      wh[1] = i8x8_to_f16(w0[2], w0[3]);
+      wh[2] = i8x8_to_f16(w1[0], w1[1]);
+      wh[3] = i8x8_to_f16(w1[2], w1[3]);
+    }
+  }
+};
+
 // v_mfma_f32_16x16x32_f16 with W as operand A.  Per 128-wide group a lane
 // loads 32 weight bytes of row n (k = 64 h + 16 q + [0, 16), h = 0, 1) and,
 // for MFMA t = 0..3, the 8 activation halves at k = 64 (t/2) + 16 q + 8 (t%2).
@@ -486,11 +546,14 @@ __device__ __forceinline__ v8h i8x8_to_f16(uint32_t lo, uint32_t hi) {
 // workgroup in dynamic LDS (M K 2 bytes, then a 256-byte zero region that
 // the fragment rows past M read), so a K block costs the weight and scale
 // loads and four LDS reads instead of four activation loads per wave.
-template <int MF, int FNW, int SK, int PF, bool XL>
-__global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __restrict__ x, const int8_t* __restrict__ W,
+// W4: INT4 weights, [N][K / 2] bytes (WFrag).
+template <int MF, int FNW, int SK, int PF, bool XL, bool W4 = false>
+__global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __restrict__ x, const uint8_t* __restrict__ W,
                                                           const float* __restrict__ ws, uint16_t* __restrict__ Y, int M,
                                                           int N, int K) {
   static_assert(!XL || MF == 1, "staged activations take one row fragment");
+  using WF = WFrag<W4>;
+  const int KW = W4 ? K >> 1 : K;   // bytes per weight row
   __shared__ v4f red[SK][64];
   extern __shared__ __attribute__((aligned(16))) char xs[];
   const int lane = threadIdx.x & 63;
@@ -500,13 +563,13 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
   const int KB = K >> 7;
 
   const int rows = N - n0 < 16 * FNW ? N - n0 : 16 * FNW;
-  const rsrc_t rw = rsrc(W + (int64_t)n0 * K, (int64_t)rows * K);
+  const rsrc_t rw = rsrc(W + (int64_t)n0 * KW, (int64_t)rows * KW);
   const rsrc_t rs = rsrc(ws + (int64_t)n0 * KB, (int64_t)rows * KB * 4);
   const rsrc_t rx = rsrc(x, (int64_t)M * K * 2);
   uint32_t woff[FNW], soff[FNW], xoff[MF];
 #pragma unroll
   for (int f = 0; f < FNW; ++f) {
-    woff[f] = (uint32_t)((f * 16 + (lane & 15)) * K + q * 16);
+    woff[f] = (uint32_t)((f * 16 + (lane & 15)) * KW + q * WF::kLaneBytes);
     soff[f] = (uint32_t)((f * 16 + 4 * q) * KB * 4);
   }
 #pragma unroll
@@ -529,16 +592,17 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < MF; ++j) facc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  v4i wv[PF][FNW][2];
+  typename WF::T wv[PF][FNW][2];
   v8h xv[PF][MF][4];
   float sv[PF][FNW][4];
   auto load = [&](int P, int g) {
-    const uint32_t ko = g < KB ? (uint32_t)g * 128u : kOob;
+    const uint32_t ko = g < KB ? (uint32_t)g * WF::kBytesPerGroup : kOob;
+    const uint32_t xk = g < KB ? (uint32_t)g * 256u : kOob;   // the group's fp16 activations
     const uint32_t so = g < KB ? (uint32_t)g * 4u : kOob;
 #pragma unroll
     for (int f = 0; f < FNW; ++f) {
-      wv[P][f][0] = bl16(rw, woff[f] + ko);
-      wv[P][f][1] = bl16(rw, woff[f] + ko + 64);
+      wv[P][f][0] = WF::load(rw, woff[f] + ko);
+      wv[P][f][1] = WF::load(rw, woff[f] + ko + WF::kBytesPerGroup / 2);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[P][f][r] = blf(rs, soff[f] + r * KB * 4 + so);
     }
@@ -551,7 +615,7 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
       for (int j = 0; j < MF; ++j)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          xv[P][j][t] = __builtin_bit_cast(v8h, bl16(rx, xoff[j] + 2 * ko + (t >> 1) * 128 + (t & 1) * 16));
+          xv[P][j][t] = __builtin_bit_cast(v8h, bl16(rx, xoff[j] + xk + (t >> 1) * 128 + (t & 1) * 16));
     }
   };
 #pragma unroll
@@ -568,10 +632,7 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
 #pragma unroll
       for (int f = 0; f < FNW; ++f) {
         v8h wh[4];
-        wh[0] = i8x8_to_f16(wv[p][f][0][0], wv[p][f][0][1]);
-        wh[1] = i8x8_to_f16(wv[p][f][0][2], wv[p][f][0][3]);
-        wh[2] = i8x8_to_f16(wv[p][f][1][0], wv[p][f][1][1]);
-        wh[3] = i8x8_to_f16(wv[p][f][1][2], wv[p][f][1][3]);
+        WF::to_f16(wv[p][f][0], wv[p][f][1], wh);
 #pragma unroll
         for (int j = 0; j < MF; ++j) {
           v4f pp = {0.f, 0.f, 0.f, 0.f};
@@ -623,11 +684,13 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
 // with the fragment layout of k_decode_w8a16.  A staged row holds 128 fp16
 // values (256 bytes, 16 chunks of 16 bytes); chunk c of row r is stored at
 // c ^ (r & 15).
-template <int MF, int NWV, int G, int PF>
+template <int MF, int NWV, int G, int PF, bool W4 = false>
 __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __restrict__ x,
-                                                           const int8_t* __restrict__ W,
+                                                           const uint8_t* __restrict__ W,
                                                            const float* __restrict__ ws, uint16_t* __restrict__ Y,
                                                            int M, int N, int K) {
+  using WF = WFrag<W4>;
+  const int KW = W4 ? K >> 1 : K;   // bytes per weight row
   constexpr int ROWS = 16 * MF;
   constexpr int CHUNKS = ROWS * 16;
   constexpr int NT = 64 * NWV;
@@ -648,10 +711,11 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
   rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
   const int nwc = rows > 0 ? nw : 0;
 
-  const rsrc_t rw = rsrc(W + (int64_t)nwc * K + kbs * 128, (int64_t)rows * K - kbs * 128);
+  const rsrc_t rw = rsrc(W + (int64_t)nwc * KW + kbs * WF::kBytesPerGroup,
+                        (int64_t)rows * KW - kbs * WF::kBytesPerGroup);
   const rsrc_t rs = rsrc(ws + (int64_t)nwc * KBt + kbs, (int64_t)rows * KBt * 4 - kbs * 4);
   const rsrc_t rx = rsrc(x + kbs * 128, (int64_t)M * K * 2 - kbs * 256);
-  const uint32_t woff = (uint32_t)((lane & 15) * K + q * 16);
+  const uint32_t woff = (uint32_t)((lane & 15) * KW + q * WF::kLaneBytes);
   const uint32_t soff = (uint32_t)(4 * q * KBt * 4);
   // activation chunk i of a group: K block xbk[i] of the group; blocks past
   // the slice's last read zero (the bytes there belong to the next slice or,
@@ -687,13 +751,13 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
     for (int i = 0; i < AG; ++i)
       if (xpos[i] >= 0) xs[buf][xpos[i]] = xreg[i];
   };
-  v4i wv[PF][2];
+  typename WF::T wv[PF][2];
   float sv[PF][4];
   auto load_w = [&](int P, int kb) {
-    const uint32_t ko = kb < KB ? (uint32_t)kb * 128u : kOob;
+    const uint32_t ko = kb < KB ? (uint32_t)kb * WF::kBytesPerGroup : kOob;
     const uint32_t so = kb < KB ? (uint32_t)kb * 4u : kOob;
-    wv[P][0] = bl16(rw, woff + ko);
-    wv[P][1] = bl16(rw, woff + ko + 64);
+    wv[P][0] = WF::load(rw, woff + ko);
+    wv[P][1] = WF::load(rw, woff + ko + WF::kBytesPerGroup / 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[P][r] = blf(rs, soff + r * KBt * 4 + so);
   };
@@ -720,10 +784,7 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
       const int buf = g & 1;
       const int bo = (p % G) * CHUNKS;
       v8h wh[4];
-      wh[0] = i8x8_to_f16(wv[p][0][0], wv[p][0][1]);
-      wh[1] = i8x8_to_f16(wv[p][0][2], wv[p][0][3]);
-      wh[2] = i8x8_to_f16(wv[p][1][0], wv[p][1][1]);
-      wh[3] = i8x8_to_f16(wv[p][1][2], wv[p][1][3]);
+      WF::to_f16(wv[p][0], wv[p][1], wh);
 #pragma unroll
       for (int j = 0; j < MF; ++j) {
         const int r = 16 * j + (lane & 15);
@@ -917,8 +978,8 @@ hipError_t decode_dispatch(const int8_t* A, const float* sa, const int8_t* W, co
   return decode_launch<MODE, 4, 2, 2, OUT>(A, sa, W, sw, Y, M, N, K, 2, st);
 }
 
-template <int MF, int FNW, int PF, bool XL>
-hipError_t w8a16_launch(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M, int64_t N, int64_t K,
+template <int MF, int FNW, int PF, bool XL, bool W4>
+hipError_t w8a16_launch(const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y, int M, int64_t N, int64_t K,
                         int waves_per_simd, hipStream_t st) {
   const int64_t wgs = (N + 16 * FNW - 1) / (16 * FNW);
   const int sk = pick_sk(wgs, K >> 7, 8, waves_per_simd);
@@ -926,43 +987,43 @@ hipError_t w8a16_launch(const uint16_t* x, const int8_t* W, const float* s, uint
   const int n = (int)N, k = (int)K;
   const size_t lds = XL ? (size_t)M * K * 2 + 256 : 0;
   switch (sk) {
-    case 8: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 8, PF, XL>), g, dim3(512), lds, st, x, W, s, Y, M, n, k); break;
-    case 4: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 4, PF, XL>), g, dim3(256), lds, st, x, W, s, Y, M, n, k); break;
-    case 2: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 2, PF, XL>), g, dim3(128), lds, st, x, W, s, Y, M, n, k); break;
-    default: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 1, PF, XL>), g, dim3(64), lds, st, x, W, s, Y, M, n, k); break;
+    case 8: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 8, PF, XL, W4>), g, dim3(512), lds, st, x, W, s, Y, M, n, k); break;
+    case 4: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 4, PF, XL, W4>), g, dim3(256), lds, st, x, W, s, Y, M, n, k); break;
+    case 2: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 2, PF, XL, W4>), g, dim3(128), lds, st, x, W, s, Y, M, n, k); break;
+    default: hipLaunchKernelGGL((k_decode_w8a16<MF, FNW, 1, PF, XL, W4>), g, dim3(64), lds, st, x, W, s, Y, M, n, k); break;
   }
   return hipGetLastError();
 }
 
-template <int MF, int NWV, int PF>
-hipError_t w8a16_shared_launch(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M, int64_t N,
+template <int MF, int NWV, int PF, bool W4>
+hipError_t w8a16_shared_launch(const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y, int M, int64_t N,
                                int64_t K, int S, hipStream_t st) {
   const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)), (unsigned)S);
-  hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2, PF>), g, dim3(64 * NWV), 0, st, x, W, s, Y, M, (int)N, (int)K);
+  hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2, PF, W4>), g, dim3(64 * NWV), 0, st, x, W, s, Y, M, (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <int MF, int NWV>
-hipError_t w8a16_shared_depth(int pf, int S, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int M,
+template <int MF, int NWV, bool W4>
+hipError_t w8a16_shared_depth(int pf, int S, const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y, int M,
                               int64_t N, int64_t K, hipStream_t st) {
   if constexpr (NWV <= 4) {
-    if (pf == 8) return w8a16_shared_launch<MF, NWV, 8>(x, W, s, Y, M, N, K, S, st);
+    if (pf == 8) return w8a16_shared_launch<MF, NWV, 8, W4>(x, W, s, Y, M, N, K, S, st);
   }
   if constexpr (NWV <= 8) {
-    if (pf >= 4) return w8a16_shared_launch<MF, NWV, 4>(x, W, s, Y, M, N, K, S, st);
+    if (pf >= 4) return w8a16_shared_launch<MF, NWV, 4, W4>(x, W, s, Y, M, N, K, S, st);
   }
-  return w8a16_shared_launch<MF, NWV, 2>(x, W, s, Y, M, N, K, S, st);
+  return w8a16_shared_launch<MF, NWV, 2, W4>(x, W, s, Y, M, N, K, S, st);
 }
 
-template <int MF>
-hipError_t w8a16_shared_width(int nwv, int pf, int S, const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y,
+template <int MF, bool W4>
+hipError_t w8a16_shared_width(int nwv, int pf, int S, const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y,
                               int M, int64_t N, int64_t K, hipStream_t st) {
   switch (nwv) {
-    case 3: return w8a16_shared_depth<MF, 3>(pf, S, x, W, s, Y, M, N, K, st);
-    case 4: return w8a16_shared_depth<MF, 4>(pf, S, x, W, s, Y, M, N, K, st);
-    case 6: return w8a16_shared_depth<MF, 6>(pf, S, x, W, s, Y, M, N, K, st);
-    case 8: return w8a16_shared_depth<MF, 8>(pf, S, x, W, s, Y, M, N, K, st);
-    default: return w8a16_shared_depth<MF, 9>(pf, S, x, W, s, Y, M, N, K, st);
+    case 3: return w8a16_shared_depth<MF, 3, W4>(pf, S, x, W, s, Y, M, N, K, st);
+    case 4: return w8a16_shared_depth<MF, 4, W4>(pf, S, x, W, s, Y, M, N, K, st);
+    case 6: return w8a16_shared_depth<MF, 6, W4>(pf, S, x, W, s, Y, M, N, K, st);
+    case 8: return w8a16_shared_depth<MF, 8, W4>(pf, S, x, W, s, Y, M, N, K, st);
+    default: return w8a16_shared_depth<MF, 9, W4>(pf, S, x, W, s, Y, M, N, K, st);
   }
 }
 
@@ -987,8 +1048,11 @@ hipError_t launch_gemm_channel_decode(const int8_t* A, const float* sa, const in
   }
 }
 
-hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
-                             int64_t K, hipStream_t st) {
+namespace {
+
+template <bool W4>
+hipError_t group16_dispatch(const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
+                           int64_t K, hipStream_t st) {
   // Per 64-row slice: up to 4 rows the split-K decode kernel with x staged in
   // LDS; 5..16 rows the shared-activation kernel when N balances over the CUs
   // (its activation stage is shared by the workgroup's waves; where N does
@@ -1025,22 +1089,34 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s,
     hipError_t e;
     if (mm >= min_shared) {
       uint16_t* dst = S > 1 ? reinterpret_cast<uint16_t*>(part) : ys;
-      e = mm <= 16 ? w8a16_shared_width<1>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
-          : mm <= 32 ? w8a16_shared_width<2>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
-                   : w8a16_shared_width<4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st);
+      e = mm <= 16 ? w8a16_shared_width<1, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+          : mm <= 32 ? w8a16_shared_width<2, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+                   : w8a16_shared_width<4, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st);
       if (e == hipSuccess && S > 1) {
         const dim3 rg((unsigned)((mm * ((N + 3) / 4) + 255) / 256));
         hipLaunchKernelGGL(k_w16_slices_sum, rg, dim3(256), 0, st, part, S, mm, (int)N, ys);
         e = hipGetLastError();
       }
     } else if (mm <= 4 && (int64_t)mm * K * 2 + 256 <= 96 * 1024) {
-      e = w8a16_launch<1, 1, 4, true>(xs, W, s, ys, mm, N, K, 3, st);
+      e = w8a16_launch<1, 1, 4, true, W4>(xs, W, s, ys, mm, N, K, 3, st);
     } else {
-      e = w8a16_launch<1, 1, 4, false>(xs, W, s, ys, mm, N, K, 3, st);
+      e = w8a16_launch<1, 1, 4, false, W4>(xs, W, s, ys, mm, N, K, 3, st);
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
+                             int64_t K, hipStream_t st) {
+  return group16_dispatch<false>(x, reinterpret_cast<const uint8_t*>(W), s, Y, M, N, K, st);
+}
+
+hipError_t launch_gemm_w4a16(const uint16_t* x, const uint8_t* W4, const float* s, uint16_t* Y, int64_t M, int64_t N,
+                             int64_t K, hipStream_t st) {
+  return group16_dispatch<true>(x, W4, s, Y, M, N, K, st);
 }
 
 }  // namespace w8

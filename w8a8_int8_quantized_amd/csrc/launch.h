@@ -60,6 +60,10 @@ hipError_t launch_gemm_asym(const int8_t* A, const float* params, const int8_t* 
                             hipStream_t st);
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* W, const float* s, uint16_t* Y, int64_t M, int64_t N,
                              int64_t K, hipStream_t st);
+hipError_t launch_gemm_w4a16(const uint16_t* x, const uint8_t* W4, const float* s, uint16_t* Y, int64_t M, int64_t N,
+                             int64_t K, hipStream_t st);
+hipError_t launch_quant_weight_int4(const void* w, bool fp16, int64_t N, int64_t K, uint8_t* q4, float* s,
+                                    hipStream_t st);
 
 // The library's own scratch (rules in workspace.h): at least `bytes` of
 // device memory for (current device, `st`, `slot`), slot 0 for split-K

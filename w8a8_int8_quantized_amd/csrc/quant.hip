@@ -48,7 +48,10 @@ __device__ __forceinline__ void unpack16_fp8(const uint4& c, float scale_inv, fl
 constexpr int kGroupRounds = 2;
 constexpr int kGroupsPerBlock = 32 * kGroupRounds;
 
-template <bool FP16>
+// I4: the INT4 weight quantiser on the same groups: scale amax / 7, codes
+// clamped to [-7, 7] and stored as offset-binary nibbles (q + 8, the even k
+// in the low nibble), 64 bytes per group, 8 per lane.
+template <bool FP16, bool I4 = false>
 __global__ __launch_bounds__(256) void k_quant_group(const uint4* __restrict__ x, int8_t* __restrict__ q,
                                                      float* __restrict__ scale, int64_t G) {
   const int j = threadIdx.x & 7;
@@ -69,6 +72,20 @@ __global__ __launch_bounds__(256) void k_quant_group(const uint4* __restrict__ x
     unpack8<FP16>(raw[r][0], v);
     unpack8<FP16>(raw[r][1], v + 8);
     float a = max8(amax_n(v, 16));
+    if constexpr (I4) {
+      const QScale sc = make_scale4(a);
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float t = fminf(fmaxf(quant_one(v[i], sc), -7.f), 7.f);
+        w[i >> 3] |= (uint32_t)((int)t + 8) << (4 * (i & 7));
+      }
+      if (gidx[r] < G) {
+        reinterpret_cast<uint2*>(q + gidx[r] * 64)[j] = make_uint2(w[0], w[1]);
+        if (j == 0) scale[gidx[r]] = sc.s;
+      }
+      continue;
+    }
     QScale sc = make_scale(a);
     float t[16];
 #pragma unroll
@@ -361,6 +378,19 @@ hipError_t launch_quant_group(const void* x, bool fp16, int64_t M, int64_t K, in
     hipLaunchKernelGGL((k_quant_group<true>), dim3((unsigned)blocks), dim3(256), 0, st, xp, q, s, G);
   else
     hipLaunchKernelGGL((k_quant_group<false>), dim3((unsigned)blocks), dim3(256), 0, st, xp, q, s, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_int4(const void* w, bool fp16, int64_t N, int64_t K, uint8_t* q4, float* s,
+                                    hipStream_t st) {
+  const int64_t G = N * (K >> 7);
+  const int64_t blocks = (G + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  const uint4* wp = static_cast<const uint4*>(w);
+  int8_t* qp = reinterpret_cast<int8_t*>(q4);
+  if (fp16)
+    hipLaunchKernelGGL((k_quant_group<true, true>), dim3((unsigned)blocks), dim3(256), 0, st, wp, qp, s, G);
+  else
+    hipLaunchKernelGGL((k_quant_group<false, true>), dim3((unsigned)blocks), dim3(256), 0, st, wp, qp, s, G);
   return hipGetLastError();
 }
 
