@@ -61,8 +61,15 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   const int8_t* Wx = W;
   const float* swx = sw;
   if (MODE == MODE_GROUPED) {
-    const int tmg = blockIdx.x / TN;
-    n0 = (blockIdx.x - tmg * TN) * BN;
+    // workgroup b runs on XCD b % 8; the TN column tiles of one expert row
+    // tile go to one XCD one after another (row tile 8 (j / TN) + b % 8,
+    // column tile j % TN, j = b / 8), so the tile's activation rows are
+    // fetched into one L2 rather than into all eight, and the XCDs take
+    // alternate row tiles (the empty ones past the last included)
+    const int j = blockIdx.x >> 3;
+    const int jt = j / TN;
+    const int tmg = 8 * jt + (blockIdx.x & 7);
+    n0 = (j - jt * TN) * BN;
     const ExpertTile g = group_tile<BM>(offsets, E, M, tmg);
     if (g.e < 0) return;
     m0 = g.r0;
@@ -500,7 +507,8 @@ hipError_t launch_gemm_block_grouped_q8(const int8_t* A, const float* sa, const 
   const int TN = (int)((N + 255) / 256);
   const bool big = P >= 96 * E;
   const int BM = big ? 256 : 128;
-  const int64_t TMmax = (P + BM - 1) / BM + E;
+  // upper bound on the number of expert row tiles, rounded up to the XCDs
+  const int64_t TMmax = ((P + BM - 1) / BM + E + 7) / 8 * 8;
   const dim3 grid((unsigned)(TMmax * TN));
   if (big)
     launch_block_kernel<MODE_GROUPED, OUT_Q8, 4>(grid, st, A, sa, W, sw, offsets, q, (int)P, (int)N, (int)K,
@@ -530,8 +538,9 @@ hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int
   const int TN = (int)((N + 255) / 256);
   const bool big = P >= 96 * E;
   const int BM = big ? 256 : 128;
-  // upper bound on the number of m-tiles over all experts
-  const int64_t TMmax = (P + BM - 1) / BM + E;
+  // upper bound on the number of m-tiles over all experts, rounded up to the
+  // XCDs (the kernel's tile order)
+  const int64_t TMmax = ((P + BM - 1) / BM + E + 7) / 8 * 8;
   const dim3 grid((unsigned)(TMmax * TN));
   if (big) {
     if (out == OUT_BF16)
