@@ -371,6 +371,36 @@ def test_grouped_moe_gemm(E, T, topk, K, N, empty, hot):
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(y))
 
 
+# From 96 rows per expert on average, experts with at most 128 rows run on
+# 128-row tiles and the others on 256-row tiles, in two launches.  Row counts
+# on both sides of the boundary (128 / 129), an empty expert, a one-row
+# expert, exactly one 256-row tile and two tiles (300 rows).
+def test_grouped_light_and_heavy_experts():
+    counts = [128, 129, 0, 1, 256, 300]
+    E, K, N = len(counts), 512, 384
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    P = int(offs[-1])
+    assert P >= 96 * E
+    x = synth.to_numpy(synth.activations(P, K, seed=21))
+    qa, sa = quant.quant_act_group(x)
+    NB = (N + 127) // 128
+    qw = np.empty((E, N, K), np.int8)
+    sw = np.empty((E, NB, K // 128), np.float32)
+    for e in range(E):
+        qw[e], sw[e] = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=200 + e)))
+    y64, y32 = gemm.gemm_block_grouped(qa, sa, qw, sw, offs)
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    OFF = torch.from_numpy(offs.astype(np.int32)).to(DEV)
+    y = _np(w8.gemm_w8a8_block_grouped(A, SA, W, SW, OFF, out_dtype=torch.float32))
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        if r1 > r0:
+            assert gemm.normwise_rel_err(y[r0:r1], y32[r0:r1]) <= 1e-5, e
+            assert gemm.normwise_rel_err(y[r0:r1], y64[r0:r1]) <= TOL64, e
+    yb = w8.gemm_w8a8_block_grouped(A, SA, W, SW, OFF, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(torch.from_numpy(y)))
+
+
 # 65..128 rows on N that balances over the CUs: the workgroup-shared decode
 # kernel with eight 16-row fragments per wave; its int32, fp32 and bf16
 # epilogues.

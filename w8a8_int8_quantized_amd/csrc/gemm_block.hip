@@ -44,7 +44,8 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
                                                              const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                              const int32_t* __restrict__ offsets, void* __restrict__ Y,
                                                              int M, int N, int K, int TM, int TN, int E,
-                                                             float* __restrict__ qs = nullptr) {
+                                                             float* __restrict__ qs = nullptr, int clo = 0,
+                                                             int chi = 0x7fffffff) {
   constexpr int BM = 64 * NWM, BN = 256, NWV = 2 * NWM;
   constexpr int STG = (BM + BN) * 128;
   constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A (= 4)
@@ -70,7 +71,9 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     const int jt = j / TN;
     const int tmg = 8 * jt + (blockIdx.x & 7);
     n0 = (j - jt * TN) * BN;
-    const ExpertTile g = group_tile<BM>(offsets, E, M, tmg);
+    // the tile lookup's three ints live in stage 1, which the first loads
+    // into it follow a barrier that every thread reaches after reading them
+    const ExpertTile g = group_tile<BM>(offsets, E, M, tmg, reinterpret_cast<int*>(smem + STG), clo, chi);
     if (g.e < 0) return;
     m0 = g.r0;
     mrows = g.r1 - g.r0;
@@ -341,9 +344,9 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
 template <int MODE, int OUT, int NWM>
 void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float* sa, const int8_t* W,
                          const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E,
-                         float* qs = nullptr) {
+                         float* qs = nullptr, int clo = 0, int chi = 0x7fffffff) {
   hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM>), grid, dim3(128 * NWM), 0, st, A, sa, W, sw, off, Y, M, N, K, TM,
-                     TN, E, qs);
+                     TN, E, qs, clo, chi);
 }
 
 // Sum of the S fp32 slices' partial tiles, in slice order, then the output.
@@ -408,6 +411,36 @@ __global__ __launch_bounds__(256) void k_splitk_sum_f32_q8(const float* __restri
   *reinterpret_cast<uint32_t*>(q + idx) =
       pack4(quant_one(o[0], sc), quant_one(o[1], sc), quant_one(o[2], sc), quant_one(o[3], sc));
   if ((threadIdx.x & 31) == 0) qs[(int64_t)m * (N >> 7) + (n >> 7)] = sc.s;
+}
+
+// The grouped (MoE) GEMM.  Every expert tile streams its expert's weight
+// panel once, so even at a few rows per expert this runs at the weight
+// stream's pace; waves whose rows are all past the expert's rows skip their
+// MFMAs.  From 96 rows per expert on average, experts with more than 128 rows
+// take 256-row tiles (one tile, one pass over the panel, up to 256 rows) and
+// the others 128-row tiles, in two launches: a 256-row tile with half its
+// row bands idle waits on its loads, a 128-row tile of four waves does not.
+// Below 96 rows per expert every expert takes 128-row tiles.  Grids are upper
+// bounds on the tile counts (expert row counts live on the device), rounded
+// to the XCDs; workgroups past the last tile return at once.
+template <int OUT>
+hipError_t grouped_launches(const int8_t* A, const float* sa, const int8_t* W, const float* sw, const int32_t* offsets,
+                            void* Y, float* qs, int64_t E, int64_t P, int64_t N, int64_t K, hipStream_t st) {
+  const int TN = (int)((N + 255) / 256);
+  auto round8 = [](int64_t t) { return (t + 7) / 8 * 8; };
+  if (P >= 96 * E) {
+    const int64_t heavy = P / 129 < E ? P / 129 : E;            // experts with more than 128 rows
+    const int64_t TM1 = round8(P / 256 + heavy + 1), TM2 = round8(P < E ? P : E);
+    launch_block_kernel<MODE_GROUPED, OUT, 4>(dim3((unsigned)(TM1 * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
+                                              (int)N, (int)K, (int)TM1, TN, (int)E, qs, 128, 0x7fffffff);
+    launch_block_kernel<MODE_GROUPED, OUT, 2>(dim3((unsigned)(TM2 * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
+                                              (int)N, (int)K, (int)TM2, TN, (int)E, qs, 0, 128);
+  } else {
+    const int64_t TM = round8((P + 127) / 128 + E);
+    launch_block_kernel<MODE_GROUPED, OUT, 2>(dim3((unsigned)(TM * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
+                                              (int)N, (int)K, (int)TM, TN, (int)E, qs);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -504,19 +537,7 @@ hipError_t launch_gemm_block_q8(const int8_t* A, const float* sa, const int8_t* 
 hipError_t launch_gemm_block_grouped_q8(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
                                         const int32_t* offsets, int8_t* q, float* qs, int64_t E, int64_t P,
                                         int64_t N, int64_t K, hipStream_t st) {
-  const int TN = (int)((N + 255) / 256);
-  const bool big = P >= 96 * E;
-  const int BM = big ? 256 : 128;
-  // upper bound on the number of expert row tiles, rounded up to the XCDs
-  const int64_t TMmax = ((P + BM - 1) / BM + E + 7) / 8 * 8;
-  const dim3 grid((unsigned)(TMmax * TN));
-  if (big)
-    launch_block_kernel<MODE_GROUPED, OUT_Q8, 4>(grid, st, A, sa, W, sw, offsets, q, (int)P, (int)N, (int)K,
-                                                 (int)TMmax, TN, (int)E, qs);
-  else
-    launch_block_kernel<MODE_GROUPED, OUT_Q8, 2>(grid, st, A, sa, W, sw, offsets, q, (int)P, (int)N, (int)K,
-                                                 (int)TMmax, TN, (int)E, qs);
-  return hipGetLastError();
+  return grouped_launches<OUT_Q8>(A, sa, W, sw, offsets, q, qs, E, P, N, K, st);
 }
 
 hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t* P, int64_t M, int64_t N, int64_t K,
@@ -530,34 +551,8 @@ hipError_t launch_gemm_block_partials(const int8_t* A, const int8_t* W, int32_t*
 hipError_t launch_gemm_block_grouped(const int8_t* A, const float* sa, const int8_t* W, const float* sw,
                                      const int32_t* offsets, void* Y, OutKind out, int64_t E, int64_t P, int64_t N,
                                      int64_t K, hipStream_t st) {
-  // Every expert tile streams its expert's weight panel once, so even at a
-  // few rows per expert this runs at the weight stream's pace; waves whose
-  // rows are all past the expert's rows skip their MFMAs.  256-row tiles from
-  // 96 rows per expert on average (fewer second tiles re-reading a panel),
-  // 128-row tiles below.
-  const int TN = (int)((N + 255) / 256);
-  const bool big = P >= 96 * E;
-  const int BM = big ? 256 : 128;
-  // upper bound on the number of m-tiles over all experts, rounded up to the
-  // XCDs (the kernel's tile order)
-  const int64_t TMmax = ((P + BM - 1) / BM + E + 7) / 8 * 8;
-  const dim3 grid((unsigned)(TMmax * TN));
-  if (big) {
-    if (out == OUT_BF16)
-      launch_block_kernel<MODE_GROUPED, OUT_BF16, 4>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
-                                                     (int)TMmax, TN, (int)E);
-    else
-      launch_block_kernel<MODE_GROUPED, OUT_F32, 4>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
-                                                    (int)TMmax, TN, (int)E);
-  } else {
-    if (out == OUT_BF16)
-      launch_block_kernel<MODE_GROUPED, OUT_BF16, 2>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
-                                                     (int)TMmax, TN, (int)E);
-    else
-      launch_block_kernel<MODE_GROUPED, OUT_F32, 2>(grid, st, A, sa, W, sw, offsets, Y, (int)P, (int)N, (int)K,
-                                                    (int)TMmax, TN, (int)E);
-  }
-  return hipGetLastError();
+  return out == OUT_BF16 ? grouped_launches<OUT_BF16>(A, sa, W, sw, offsets, Y, nullptr, E, P, N, K, st)
+                         : grouped_launches<OUT_F32>(A, sa, W, sw, offsets, Y, nullptr, E, P, N, K, st);
 }
 
 }  // namespace w8

@@ -55,37 +55,36 @@ constexpr unsigned kChOob = 0x20000000u;   // added to a load's offset: past eve
 // q - 128, prm = {s, z}, wsum = per-row weight sums) in place of the
 // channel-wise one: Y = fp32(fp32(s * sw[n]) * fp32(fp32(ACC + 128 WS[n]) -
 // fp32(z * fp32(WS[n])))).
-// HALF (int32 output, M <= 128, FN = 8): tile rows 128..255 lie past M, so
-// waves 4..7 (whose 64-row bands those are) issue only their share of the
-// stage loads and meet the barriers; their SIMDs then run one MFMA wave each
-// and the tile's MFMA work halves.  With half the MFMA work a K block no
-// longer covers the load latency of the next one, so these tiles keep three
-// stages in the same 160 KB (a stage's A tile needs only 128 rows): stage 0
-// at A 0 K / W 32 K, stage 1 at A 64 K / W 96 K, stage 2 at A 16 K / W 128 K,
-// the junk kilobyte at 80 K; the loads of rows 128..255 go to the junk
-// kilobyte, so every wave still issues eight loads per block, and a barrier
-// waits for the older of two blocks in flight.
-template <int OUT, int FN, bool AS = false, bool HALF = false>
+// SKINNY (int32 output, M <= 128, FN = 4): a 128 (m) x 256 (n) tile on the
+// eight waves as 4 (n) x 2 (m), each wave 64 x 64 (4 x 4 fragments), so every
+// SIMD keeps two MFMA waves on rows that exist (a 256-row tile would leave
+// half its row bands empty, one MFMA wave per SIMD waiting on its LDS reads).
+// A stage is 48 KB (A 128 rows, W 256 rows), so three fit: a barrier waits
+// for the older of two blocks in flight, six loads per wave per block.
+template <int OUT, int FN, bool AS = false, bool SKINNY = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                          void* __restrict__ Y, int M, int N, int K, int TM, int GM,
                                                          const float* __restrict__ prm = nullptr,
                                                          const int32_t* __restrict__ wsum = nullptr) {
-  static_assert(!HALF || FN == 8, "HALF: 256-column tiles");
-  constexpr int BN = 32 * FN;
-  constexpr int kStage = (kChBM + BN) * 128;
-  constexpr int kJunk = HALF ? 80 * 1024 : 2 * kStage;
-  // two stages and the junk kilobyte, or the bf16 epilogue's 256 rows of 512
-  // B; HALF: three stages, the whole 160 KB
-  constexpr int kSmem = HALF ? 160 * 1024 : (kJunk + 1024 > kChBM * 512 ? kJunk + 1024 : kChBM * 512);
+  static_assert(!SKINNY || (FN == 4 && OUT == OUT_I32 && !AS), "SKINNY: int32 128 x 256 tiles");
+  constexpr int NWN = SKINNY ? 4 : 2;            // waves along n
+  constexpr int BM = SKINNY ? 128 : kChBM;       // tile rows
+  constexpr int BN = NWN * 16 * FN;
+  constexpr int NST = SKINNY ? 3 : 2;            // stages in the ring
+  constexpr int LPB = SKINNY ? 6 : 8;            // loads per wave per block
+  constexpr int kStage = (BM + BN) * 128;
+  constexpr int kJunk = NST * kStage;
+  // the stages and the junk kilobyte, or the bf16 epilogue's 256 rows of 512 B
+  constexpr int kSmem = kJunk + 1024 > kChBM * 512 || SKINNY ? kJunk + 1024 : kChBM * 512;
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % NWN, wm = wave / NWN;
   int tm, tn;
   strip_tile(blockIdx.x, TM, (int)gridDim.x / TM, GM, tm, tn);
-  const int m0 = tm * kChBM, n0 = tn * BN;
-  const int mval = M - m0 < kChBM ? M - m0 : kChBM;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int mval = M - m0 < BM ? M - m0 : BM;
   const int nval = N - n0 < BN ? N - n0 : BN;
   // split-K: slice blockIdx.y of gridDim.y covers K blocks kbs .. kbe - 1 and
   // writes its raw int32 tile to slice blockIdx.y of Y (M x N each)
@@ -109,15 +108,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restric
   const int soff0 = wave * K8;
   const uint32_t dlds0 = lds0 + wave * 1024;
   const uint32_t ljunk = lds0 + kJunk;
-  // HALF: byte offsets of block t's A and W tiles in the three-stage ring
-  auto st_a = [](int t) -> uint32_t {
-    const int m = t % 3;
-    return m == 0 ? 0u : (m == 1 ? 65536u : 16384u);
-  };
-  auto st_w = [](int t) -> uint32_t {
-    const int m = t % 3;
-    return m == 0 ? 32768u : (m == 1 ? 98304u : 131072u);
-  };
 
   v4i acc[FN][4];
 #pragma unroll
@@ -126,13 +116,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restric
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
 #define CH_LOAD(T, D, SO)                                                                          \
-  if constexpr (HALF) {                                                                           \
-    if ((D) >= 2 && (D) < 4)                                                                      \
-      dma16(ra, voff, soff0 + 8 * (D) * K8 + (T) * 128 + (SO) + kChOob, ljunk);                   \
-    else if ((D) < 4)                                                                             \
-      dma16(ra, voff, soff0 + 8 * (D) * K8 + (T) * 128 + (SO), dlds0 + st_a(T) + 8 * (D) * 1024);  \
+  if constexpr (SKINNY) {                                                                         \
+    const uint32_t base = dlds0 + ((T) % 3) * kStage;                                             \
+    if ((D) < 2)                                                                                  \
+      dma16(ra, voff, soff0 + 8 * (D) * K8 + (T) * 128 + (SO), base + 8 * (D) * 1024);            \
     else                                                                                          \
-      dma16(rw, voff, soff0 + 8 * ((D) - 4) * K8 + (T) * 128 + (SO), dlds0 + st_w(T) + 8 * ((D) - 4) * 1024); \
+      dma16(rw, voff, soff0 + 8 * ((D) - 2) * K8 + (T) * 128 + (SO), base + BM * 128 + 8 * ((D) - 2) * 1024); \
   } else {                                                                                        \
     const uint32_t base = dlds0 + ((T) & 1) * kStage;                                             \
     if ((D) < 4) {                                                                                \
@@ -145,9 +134,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restric
     }                                                                                             \
   }
 #define CH_READ(BLK, LO, WF, AF, R)                                                                \
-  if constexpr (HALF) {                                                                           \
-    if ((R) < 4) AF[(R)] = *(const v4i*)(smem + st_a(BLK) + (wm * 64 + (R) * 16) * 128 + (LO));   \
-    else WF[(R) - 4] = *(const v4i*)(smem + st_w(BLK) + (wn * 16 * FN + ((R) - 4) * 16) * 128 + (LO)); \
+  if constexpr (SKINNY) {                                                                         \
+    const char* buf = smem + ((BLK) % 3) * kStage;                                                \
+    if ((R) < 4) AF[(R)] = *(const v4i*)(buf + (wm * 64 + (R) * 16) * 128 + (LO));                \
+    else WF[(R) - 4] = *(const v4i*)(buf + BM * 128 + (wn * 16 * FN + ((R) - 4) * 16) * 128 + (LO)); \
   } else {                                                                                        \
     const char* buf = smem + ((BLK) & 1) * kStage;                                                \
     if ((R) < 4) AF[(R)] = *(const v4i*)(buf + (wm * 64 + (R) * 16) * 128 + (LO));                \
@@ -162,7 +152,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restric
       CH_READ(RBLK, RLO, WN_, AN_, 2 * g)                                                         \
       if (2 * g + 1 < 4 + FN) CH_READ(RBLK, RLO, WN_, AN_, 2 * g + 1)                             \
     }                                                                                             \
-    if ((LD) && g < 4) {                                                                          \
+    if ((LD) && 2 * g < LPB) {                                                                    \
       CH_LOAD(LT, 2 * g, LSO)                                                                     \
       CH_LOAD(LT, 2 * g + 1, LSO)                                                                 \
     }                                                                                             \
@@ -171,41 +161,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restric
     __builtin_amdgcn_sched_barrier(0);                                                            \
   }
 
-  if (HALF && wave >= 4) {
-    // the same loads and barriers as the MFMA waves below, nothing else;
-    // their rows are never stored (int32 output only)
-    static_assert(!HALF || (OUT == OUT_I32 && !AS), "HALF: int32 output only");
+  // prologue: block 0 loaded and visible, block 1 (SKINNY: blocks 1 and 2)
+  // in flight
 #pragma unroll
-    for (int d = 0; d < 8; ++d) CH_LOAD(0, d, 0u)
-    {
-      const unsigned so1 = 1 < NK ? 0u : kChOob, so2 = 2 < NK ? 0u : kChOob;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) CH_LOAD(1, d, so1)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) CH_LOAD(2, d, so2)
-    }
-    wait_barrier<16, 15>();
-    for (int kb = 0; kb + 1 < NK; ++kb) {
-      wait_barrier<8, 0>();
-      const unsigned so = kb + 3 < NK ? 0u : kChOob;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) CH_LOAD(kb + 3, d, so)
-    }
-    waitcnt<0, 0>();
-    return;
-  }
-
-  // prologue: block 0 loaded and visible, block 1 (HALF: blocks 1 and 2) in
-  // flight
-#pragma unroll
-  for (int d = 0; d < 8; ++d) CH_LOAD(0, d, 0u)
-  if constexpr (HALF) {
+  for (int d = 0; d < LPB; ++d) CH_LOAD(0, d, 0u)
+  if constexpr (SKINNY) {
     const unsigned so1 = 1 < NK ? 0u : kChOob, so2 = 2 < NK ? 0u : kChOob;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) CH_LOAD(1, d, so1)
+    for (int d = 0; d < LPB; ++d) CH_LOAD(1, d, so1)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) CH_LOAD(2, d, so2)
-    wait_barrier<16, 15>();
+    for (int d = 0; d < LPB; ++d) CH_LOAD(2, d, so2)
+    wait_barrier<2 * LPB, 15>();
   } else {
     wait_barrier<0, 15>();
     const unsigned so1 = 1 < NK ? 0u : kChOob;
@@ -215,14 +181,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_channel(const int8_t* __restric
   v4i w0[FN], a0[4], w1[FN], a1[4];
 #pragma unroll
   for (int r = 0; r < 4 + FN; ++r) CH_READ(0, lo0, w0, a0, r)
-  // the block loaded in step B: the one two (HALF: three) ahead, into the
+  // the block loaded in step B: the one two (SKINNY: three) ahead, into the
   // stage block kb has just left
-  constexpr int kAhead = HALF ? 3 : 2;
+  constexpr int kAhead = SKINNY ? 3 : 2;
   for (int kb = 0; kb + 1 < NK; ++kb) {
     CH_STEP(w0, a0, true, kb, lo1, w1, a1, false, 0, 0u)
-    // block kb + 1 has landed everywhere (HALF: block kb + 2 may still be in
-    // flight); every wave is past its reads of kb
-    wait_barrier<HALF ? 8 : 0, 0>();
+    // block kb + 1 has landed everywhere (SKINNY: block kb + 2 may still be
+    // in flight); every wave is past its reads of kb
+    wait_barrier<SKINNY ? LPB : 0, 0>();
     const unsigned so = kb + kAhead < NK ? 0u : kChOob;
     CH_STEP(w1, a1, true, kb + 1, lo0, w0, a0, true, kb + kAhead, so)
   }
@@ -549,7 +515,7 @@ hipError_t channel_split(const int8_t* A, const float* sa, const int8_t* W, cons
   const int TM = (int)((M + kChBM - 1) / kChBM), TN = (int)((N + 255) / 256);
   const dim3 grid((unsigned)(TM * TN), (unsigned)S);
   if (M <= 128)
-    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8, false, true>), grid, dim3(512), 0, st, A, sa, W, sw, ws, (int)M,
+    hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 4, false, true>), grid, dim3(512), 0, st, A, sa, W, sw, ws, (int)M,
                        (int)N, (int)K, TM, channel_strip(TM));
   else
     hipLaunchKernelGGL((k_gemm_channel<OUT_I32, 8>), grid, dim3(512), 0, st, A, sa, W, sw, ws, (int)M, (int)N, (int)K,

@@ -20,10 +20,13 @@ struct ExpertTile {
 
 // Wave 0 counts the tiles of E / 64 experts per lane, prefix-sums the counts
 // across the wave and lets the lane whose range holds tile t walk to it.
-// Every thread of the workgroup must call it (it ends with a barrier).
+// Only experts with more than clo and at most chi rows have tiles (the others
+// count zero), so one launch can take the light experts and another the
+// heavy ones.  Every thread of the workgroup must call it (it ends with a
+// barrier); sel is three ints of LDS that the caller leaves alone until every
+// thread has returned.
 template <int BM>
-__device__ ExpertTile group_tile(const int32_t* __restrict__ off, int E, int P, int t) {
-  __shared__ int sel[3];
+__device__ ExpertTile group_tile(const int32_t* __restrict__ off, int E, int P, int t, int* sel, int clo, int chi) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (E + 63) / 64;
@@ -34,7 +37,7 @@ __device__ ExpertTile group_tile(const int32_t* __restrict__ off, int E, int P, 
       int lo = off[e], hi = off[e + 1];
       lo = lo < 0 ? 0 : (lo > P ? P : lo);
       hi = hi < lo ? lo : (hi > P ? P : hi);
-      cnt += (hi - lo + BM - 1) / BM;
+      if (hi - lo > clo && hi - lo <= chi) cnt += (hi - lo + BM - 1) / BM;
     }
     int inc = cnt;
 #pragma unroll
@@ -49,7 +52,7 @@ __device__ ExpertTile group_tile(const int32_t* __restrict__ off, int E, int P, 
         int lo = off[e], hi = off[e + 1];
         lo = lo < 0 ? 0 : (lo > P ? P : lo);
         hi = hi < lo ? lo : (hi > P ? P : hi);
-        const int c = (hi - lo + BM - 1) / BM;
+        const int c = hi - lo > clo && hi - lo <= chi ? (hi - lo + BM - 1) / BM : 0;
         if (t < acc + c) {
           const int r0 = lo + (t - acc) * BM;
           sel[0] = e;
