@@ -39,14 +39,21 @@ constexpr int kTileCUs = 256;   // compute units the tile grids are sized agains
 // MODE_GROUPED: the rows of A / Y are expert-sorted (offsets), W and w_scale
 // hold E experts; tile b / TN is the expert tile number.
 // MODE_PARTIALS: Y gets every K block's raw int32 partial, Y[kb][m][n].
-template <int MODE, int OUT, int NWM>
-__global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
+// NWN: waves along n.  2: each wave 128 (n) x 64 (m), 4 x 2 chains; 4 (with
+// NWM = 2): a 128 x 256 tile on eight waves, each 64 (n) x 64 (m), 2 x 2
+// chains, so that 128-row tiles keep two MFMA waves per SIMD (bf16 / fp32
+// output: a wave's 64 columns are half a quantisation group).
+template <int MODE, int OUT, int NWM, int NWN = 2>
+__global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                              const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                              const int32_t* __restrict__ offsets, void* __restrict__ Y,
                                                              int M, int N, int K, int TM, int TN, int E,
                                                              float* __restrict__ qs = nullptr, int clo = 0,
                                                              int chi = 0x7fffffff) {
-  constexpr int BM = 64 * NWM, BN = 256, NWV = 2 * NWM;
+  static_assert(NWN == 2 || (NWN == 4 && OUT != OUT_Q8), "a Q8 group is one wave's 128 columns");
+  constexpr int BM = 64 * NWM, BN = 256, NWV = NWN * NWM;
+  constexpr int CI = BN / (32 * NWN);   // 32-column chains per wave along n
+  constexpr int WC = 32 * CI;           // columns per wave
   constexpr int STG = (BM + BN) * 128;
   constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A (= 4)
   constexpr int WI = BN / (8 * NWV);   // ... and for W
@@ -54,7 +61,7 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   __shared__ __attribute__((aligned(1024))) char smem[2 * STG];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % NWN, wm = wave / NWN;
   const int KB = K >> 7;
   const int NB = (N + 127) >> 7;
 
@@ -104,9 +111,9 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) lo[ks] = frag_off(lane & 31, 2 * ks + (lane >> 5));   // 32x32x32 operand
 
-  // this wave's 128 columns lie in one 128-wide N block: one weight scale per
+  // this wave's columns lie in one 128-wide N block: one weight scale per
   // K block; rows past the tile read the last row's scales (never stored)
-  int nbw = (n0 + wn * 128) >> 7;
+  int nbw = (n0 + wn * WC) >> 7;
   nbw = nbw < NB ? nbw : NB - 1;
   const float* sw_row = swx + (int64_t)nbw * KB + kbs;
   const float* sa_t = sa + (int64_t)m0 * KB + kbs;   // uniform base, 32-bit lane offsets
@@ -117,9 +124,9 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     sao[j] = (r < mrows ? r : mrows - 1) * KB;
   }
 
-  v4f facc[4][2][4];
+  v4f facc[CI][2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < CI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -130,7 +137,9 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   // with scale s, or store it raw
   auto drain = [&](const v16i& p, auto ic, auto jc, float s, int kbp) {
     constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-    if (DQ) {
+    if constexpr (i >= CI) {
+      return;
+    } else if (DQ) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
         const int m = m0 + ml;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 128 + i * 32 + g * 8 + 4 * (lane >> 5);
+          const int n = n0 + wn * WC + i * 32 + g * 8 + 4 * (lane >> 5);
           if (n < N)
             store4i(static_cast<int32_t*>(Y) + ((int64_t)(kbs + kbp) * M + m) * N + n, n, N, vec,
                     (v4i){p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]});
@@ -194,21 +203,21 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) af[j][ks] = *(const v4i*)(buf + (wm * 64 + j * 32) * 128 + lo[ks]);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wc[ks] = *(const v4i*)(buf + BM * 128 + (wn * 128) * 128 + lo[ks]);
+    for (int ks = 0; ks < 4; ++ks) wc[ks] = *(const v4i*)(buf + BM * 128 + (wn * WC) * 128 + lo[ks]);
     // chain t = 2 i + j
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 2 * CI; ++t) {
       const int i = t >> 1, j = t & 1;
-      if (j == 0 && i < 3) {
+      if (j == 0 && i < CI - 1) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          wnx[ks] = *(const v4i*)(buf + BM * 128 + (wn * 128 + (i + 1) * 32) * 128 + lo[ks]);
+          wnx[ks] = *(const v4i*)(buf + BM * 128 + (wn * WC + (i + 1) * 32) * 128 + lo[ks]);
       }
       v16i c = {};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_i32_32x32x32_i8(wc[ks], af[j][ks], c, 0, 0, 0);
       if (t == 0) {
-        if (kb > 0) drain(pp, std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}, sp, kb - 1);
+        if (kb > 0) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, kb - 1);
       } else if (t & 1) {   // previous chain: (i, 0)
         if (i == 0) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, sc0, kb);
         if (i == 1) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sc0, kb);
@@ -225,11 +234,11 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
       for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        if (j == 0 && i < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (j == 0 && i < CI - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       pp = c;
-      if (j == 1 && i < 3) {
+      if (j == 1 && i < CI - 1) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) wc[ks] = wnx[ks];
       }
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     sp = sc1;
   }
 #undef BK_DMA
-  if (NK > 0 && wact) drain(pp, std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}, sp, NK - 1);
+  if (NK > 0 && wact) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, NK - 1);
   waitcnt<0, 0>();
   if (!DQ) return;
 
@@ -290,26 +299,28 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     for (int j = 0; j < 2; ++j) {
       const int r = wm * 64 + j * 32 + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < CI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint32_t h[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(facc[i][j][g][q]);
-          const int chunk = wn * 16 + i * 4 + g;
+          const int chunk = wn * 4 * CI + i * 4 + g;
           *reinterpret_cast<uint2*>(smem + r * 512 + ((chunk ^ (r & 15)) << 4) + 8 * (lane >> 5)) =
               make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
     }
     waitcnt<63, 0>();
     barrier();
-    // wave w stores tile rows 32 w .. 32 w + 31, two rows per instruction
+    // wave w stores tile rows RPW w .. RPW w + RPW - 1, two rows per
+    // instruction
+    constexpr int RPW = BM / NWV;
     const int cl = lane & 31;
     const int n = n0 + 8 * cl;
     const bool vec8 = (N & 7) == 0 && n + 7 < N;
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int r = wave * 32 + 2 * it + (lane >> 5);
+    for (int it = 0; it < RPW / 2; ++it) {
+      const int r = wave * RPW + 2 * it + (lane >> 5);
       const v4i v = *reinterpret_cast<const v4i*>(smem + r * 512 + ((cl ^ (r & 15)) << 4));
       if (r >= mrows || n >= N) continue;
       uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)(m0 + r) * N + n;
@@ -330,10 +341,10 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
     if (ml >= mrows) continue;
     const int m = m0 + ml;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < CI; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + i * 32 + g * 8 + 4 * (lane >> 5);
+        const int n = n0 + wn * WC + i * 32 + g * 8 + 4 * (lane >> 5);
         if (n >= N) continue;
         store4<OUT>(Y, (int64_t)m * N + n, n, N, vec, facc[i][j][g][0], facc[i][j][g][1], facc[i][j][g][2],
                     facc[i][j][g][3]);
@@ -341,12 +352,12 @@ __global__ __launch_bounds__(128 * NWM, 1) void k_gemm_block(const int8_t* __res
   }
 }
 
-template <int MODE, int OUT, int NWM>
+template <int MODE, int OUT, int NWM, int NWN = 2>
 void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float* sa, const int8_t* W,
                          const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E,
                          float* qs = nullptr, int clo = 0, int chi = 0x7fffffff) {
-  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM>), grid, dim3(128 * NWM), 0, st, A, sa, W, sw, off, Y, M, N, K, TM,
-                     TN, E, qs, clo, chi);
+  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM, NWN>), grid, dim3(64 * NWM * NWN), 0, st, A, sa, W, sw, off, Y, M,
+                     N, K, TM, TN, E, qs, clo, chi);
 }
 
 // Sum of the S fp32 slices' partial tiles, in slice order, then the output.
@@ -427,17 +438,19 @@ template <int OUT>
 hipError_t grouped_launches(const int8_t* A, const float* sa, const int8_t* W, const float* sw, const int32_t* offsets,
                             void* Y, float* qs, int64_t E, int64_t P, int64_t N, int64_t K, hipStream_t st) {
   const int TN = (int)((N + 255) / 256);
+  // (four waves: eight waves as 4 x 2 measured 3-4 % slower on the MoE rows)
+  constexpr int NWN2 = 2;
   auto round8 = [](int64_t t) { return (t + 7) / 8 * 8; };
   if (P >= 96 * E) {
     const int64_t heavy = P / 129 < E ? P / 129 : E;            // experts with more than 128 rows
     const int64_t TM1 = round8(P / 256 + heavy + 1), TM2 = round8(P < E ? P : E);
     launch_block_kernel<MODE_GROUPED, OUT, 4>(dim3((unsigned)(TM1 * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
                                               (int)N, (int)K, (int)TM1, TN, (int)E, qs, 128, 0x7fffffff);
-    launch_block_kernel<MODE_GROUPED, OUT, 2>(dim3((unsigned)(TM2 * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
+    launch_block_kernel<MODE_GROUPED, OUT, 2, NWN2>(dim3((unsigned)(TM2 * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
                                               (int)N, (int)K, (int)TM2, TN, (int)E, qs, 0, 128);
   } else {
     const int64_t TM = round8((P + 127) / 128 + E);
-    launch_block_kernel<MODE_GROUPED, OUT, 2>(dim3((unsigned)(TM * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
+    launch_block_kernel<MODE_GROUPED, OUT, 2, NWN2>(dim3((unsigned)(TM * TN)), st, A, sa, W, sw, offsets, Y, (int)P,
                                               (int)N, (int)K, (int)TM, TN, (int)E, qs);
   }
   return hipGetLastError();
@@ -450,9 +463,9 @@ hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, 
   if (decode_path_takes(M, N, false)) return launch_gemm_block_decode(A, sa, W, sw, Y, out, M, N, K, st);
   const int TN = (int)((N + 255) / 256);
   // 128-row tiles for few rows, and where 256-row tiles would leave CUs idle
-  // (twice the tiles before any K split, one wave per SIMD: DeepSeek's q_a
-  // and kv_a projections at 4096 tokens run 11-14 % faster than on split
-  // 256-row tiles)
+  // (twice the tiles before any K split: DeepSeek's q_a and kv_a projections
+  // at 4096 tokens run 11-14 % faster than on split 256-row tiles), on eight
+  // waves as 4 (n) x 2 (m) (two MFMA waves per SIMD: another 4-5 %)
   const int BM = (M <= 128 || ((M + 255) / 256) * TN < kTileCUs) ? 128 : 256;
   const int TM = (int)((M + BM - 1) / BM);
   // ~2.6 us per 256 x 256 tile and K block (1.7 for 128 x 256) at the
@@ -466,11 +479,11 @@ hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, 
   const bool f32 = S > 1 || out == OUT_F32;
   if (BM == 128) {
     if (f32)
-      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM,
-                                                    TN, 0);
+      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K,
+                                                       TM, TN, 0);
     else
-      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM,
-                                                     TN, 0);
+      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K,
+                                                        TM, TN, 0);
   } else {
     if (f32)
       launch_block_kernel<MODE_DEQUANT, OUT_F32, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K, TM,
@@ -523,7 +536,7 @@ hipError_t launch_gemm_block_q8(const int8_t* A, const float* sa, const int8_t* 
   const WsLease lease = stream_workspace(st, 0, (size_t)S * M * N * 4);
   if (lease.status() != kWsOk) return ws_error(lease);
   if (BM == 128)
-    launch_block_kernel<MODE_DEQUANT, OUT_F32, 2>(grid, st, A, sa, W, sw, nullptr, lease.ptr(), (int)M, (int)N, (int)K,
+    launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 4>(grid, st, A, sa, W, sw, nullptr, lease.ptr(), (int)M, (int)N, (int)K,
                                                   TM, TN, 0);
   else
     launch_block_kernel<MODE_DEQUANT, OUT_F32, 4>(grid, st, A, sa, W, sw, nullptr, lease.ptr(), (int)M, (int)N, (int)K,
