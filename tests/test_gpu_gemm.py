@@ -133,6 +133,26 @@ def test_block_gemm(M, N, K):
     assert gemm.normwise_rel_err(_np(yb.float()), y64) <= TOL64
 
 
+# The 128-row tile widths of the block-wise GEMM, picked by the launch model:
+# 128 x 192 tiles (four waves, a weight scale per 32-column chain since a
+# wave's 96 columns can straddle two 128-column scale blocks) where the tiles
+# do not fill the CUs, unsplit (300 x 1000) and split over K (3 and 10
+# slices); 128 x 256 tiles on eight waves where they take more than one
+# round, unsplit (1500 x 5000) and split (200 x 9000, 3 slices).  M and N
+# are ragged in every case.
+@pytest.mark.parametrize("M,N,K", [(300, 1000, 512), (1000, 1500, 3072), (257, 700, 4096), (1500, 5000, 256),
+                                   (200, 9000, 4096)])
+def test_block_gemm_tile_widths(M, N, K):
+    qa, sa, qw, sw = _inputs(M, N, K, seed=M + N, scheme="block")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    _, y64, y32 = gemm.gemm_block(qa, sa, qw, sw)
+    yf = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    e32, e64 = gemm.normwise_rel_err(_np(yf), y32), gemm.normwise_rel_err(_np(yf), y64)
+    assert e32 <= 1e-5 and e64 <= TOL64, (e32, e64)
+    yb = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+
+
 def test_block_equals_channel_when_k_is_one_block():
     M, N, K = 70, 256, 128
     qa, sa, qw, sw = _inputs(M, N, K, seed=1, scheme="block")

@@ -8,7 +8,8 @@
 //
 // Tile: 256 (n) x BM (m), BM = 64 NWM, 2 NWM waves in a 2 (n) x NWM (m) grid,
 // each wave 128 (n) x 64 (m) as 4 x 2 fragments ("chains") of
-// v_mfma_i32_32x32x32_i8; a chain is four MFMAs over one K block (its exact
+// v_mfma_i32_32x32x32_i8 (128-row tiles also come as 256 x 128 on eight
+// waves of 64 x 64 and as 192 x 128 on four waves of 96 x 64); a chain is four MFMAs over one K block (its exact
 // int32 P), then 16 cvt + 16 fma per lane dequantise it into the wave's fp32
 // accumulators, which stay in VGPRs.  Operands stream global -> LDS through
 // direct-to-LDS loads into a two-slot ring (pipeline.h), one K block per slot.
@@ -43,7 +44,11 @@ constexpr int kTileCUs = 256;   // compute units the tile grids are sized agains
 // NWM = 2): a 128 x 256 tile on eight waves, each 64 (n) x 64 (m), 2 x 2
 // chains, so that 128-row tiles keep two MFMA waves per SIMD (bf16 / fp32
 // output: a wave's 64 columns are half a quantisation group).
-template <int MODE, int OUT, int NWM, int NWN = 2>
+// BN: tile width, 256 or 192 (with NWM = NWN = 2: a 128 x 192 tile on four
+// waves of 96 (n) x 64 (m), 3 x 2 chains; a wave's columns may then straddle
+// two 128-column weight-scale blocks, so each 32-column chain takes its own
+// weight scale).
+template <int MODE, int OUT, int NWM, int NWN = 2, int BN = 256>
 __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                              const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                              const int32_t* __restrict__ offsets, void* __restrict__ Y,
@@ -51,9 +56,14 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
                                                              float* __restrict__ qs = nullptr, int clo = 0,
                                                              int chi = 0x7fffffff) {
   static_assert(NWN == 2 || (NWN == 4 && OUT != OUT_Q8), "a Q8 group is one wave's 128 columns");
-  constexpr int BM = 64 * NWM, BN = 256, NWV = NWN * NWM;
+  static_assert(BN == 256 || (BN == 192 && NWM == 2 && NWN == 2 && MODE == MODE_DEQUANT && OUT != OUT_Q8),
+                "192-wide tiles: dense, 128 rows, four waves, bf16 / fp32 output");
+  constexpr int BM = 64 * NWM, NWV = NWN * NWM;
   constexpr int CI = BN / (32 * NWN);   // 32-column chains per wave along n
   constexpr int WC = 32 * CI;           // columns per wave
+  // weight scales per wave and K block: one where the wave's columns lie in
+  // one 128-wide N block, else one per chain
+  constexpr int NSW = (128 % WC) == 0 ? 1 : CI;
   constexpr int STG = (BM + BN) * 128;
   constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A (= 4)
   constexpr int WI = BN / (8 * NWV);   // ... and for W
@@ -111,11 +121,15 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) lo[ks] = frag_off(lane & 31, 2 * ks + (lane >> 5));   // 32x32x32 operand
 
-  // this wave's columns lie in one 128-wide N block: one weight scale per
-  // K block; rows past the tile read the last row's scales (never stored)
-  int nbw = (n0 + wn * WC) >> 7;
-  nbw = nbw < NB ? nbw : NB - 1;
-  const float* sw_row = swx + (int64_t)nbw * KB + kbs;
+  // the weight-scale row of each 128-wide N block the wave's chains lie in;
+  // rows past the tile read the last row's scales (never stored)
+  const float* sw_row[NSW];
+#pragma unroll
+  for (int q = 0; q < NSW; ++q) {
+    int nbw = (n0 + wn * WC + 32 * q) >> 7;
+    nbw = nbw < NB ? nbw : NB - 1;
+    sw_row[q] = swx + (int64_t)nbw * KB + kbs;
+  }
   const float* sa_t = sa + (int64_t)m0 * KB + kbs;   // uniform base, 32-bit lane offsets
   int sao[2];
 #pragma unroll
@@ -172,14 +186,19 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
       dma16(rw, voffW, b * K8 + (T) * 128, base + BM * 128 + (wave * WI + b) * 1024);             \
   }
 
+  // weight-scale index of chain i (i past the last chain: never drained)
+#define QI(i) (NSW == 1 || (i) >= NSW ? 0 : (i))
   const int NK = kbe - kbs;   // K blocks of this slice, numbered from its first
   // scales of the next block to compute (loaded one block ahead), and the
   // pending chain: chain 7 (i = 3, j = 1) of the previous block
-  float la0 = 0.f, la1 = 0.f, lw = 0.f;
+  float la0 = 0.f, la1 = 0.f, lw[NSW];
+#pragma unroll
+  for (int q = 0; q < NSW; ++q) lw[q] = 0.f;
   if (DQ && NK > 0) {
     la0 = sa_t[sao[0]];
     la1 = sa_t[sao[1]];
-    lw = sw_row[0];
+#pragma unroll
+    for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][0];
   }
   float sp = 0.f;
   v16i pp = {};
@@ -188,12 +207,20 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
     waitcnt<0, 0>();   // block kb and its scales landed; own reads of kb-1 done
     barrier();         // everyone's block kb landed; everyone is past kb-1
     if (kb + 1 < NK) BK_DMA(kb + 1)
-    const float sc0 = __fmul_rn(la0, lw), sc1 = __fmul_rn(la1, lw);
+    // scale of chain (i, j): sc0[i] for j = 0, sc1[i] for j = 1 (index 0
+    // when the wave has one weight scale)
+    float sc0[NSW], sc1[NSW];
+#pragma unroll
+    for (int q = 0; q < NSW; ++q) {
+      sc0[q] = __fmul_rn(la0, lw[q]);
+      sc1[q] = __fmul_rn(la1, lw[q]);
+    }
     if (DQ) {
       const int kn = kb + 1 < NK ? kb + 1 : kb;
       la0 = sa_t[sao[0] + kn];
       la1 = sa_t[sao[1] + kn];
-      lw = sw_row[kn];
+#pragma unroll
+      for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][kn];
     }
     if (!wact) continue;
     const char* buf = smem + (kb & 1) * STG;
@@ -219,14 +246,14 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
       if (t == 0) {
         if (kb > 0) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, kb - 1);
       } else if (t & 1) {   // previous chain: (i, 0)
-        if (i == 0) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, sc0, kb);
-        if (i == 1) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sc0, kb);
-        if (i == 2) drain(pp, std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{}, sc0, kb);
-        if (i == 3) drain(pp, std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{}, sc0, kb);
+        if (i == 0) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, sc0[0], kb);
+        if (i == 1) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sc0[QI(1)], kb);
+        if (i == 2) drain(pp, std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{}, sc0[QI(2)], kb);
+        if (i == 3) drain(pp, std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{}, sc0[QI(3)], kb);
       } else {              // previous chain: (i - 1, 1)
-        if (i == 1) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, sc1, kb);
-        if (i == 2) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, sc1, kb);
-        if (i == 3) drain(pp, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}, sc1, kb);
+        if (i == 1) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, sc1[0], kb);
+        if (i == 2) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, sc1[QI(1)], kb);
+        if (i == 3) drain(pp, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}, sc1[QI(2)], kb);
       }
       // one MFMA, then eight VALU ops, four times; the next pair's W reads
       // ride along
@@ -243,9 +270,10 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
         for (int ks = 0; ks < 4; ++ks) wc[ks] = wnx[ks];
       }
     }
-    sp = sc1;
+    sp = sc1[QI(CI - 1)];
   }
 #undef BK_DMA
+#undef QI
   if (NK > 0 && wact) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, NK - 1);
   waitcnt<0, 0>();
   if (!DQ) return;
@@ -291,9 +319,11 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
     return;
   }
   if (OUT == OUT_BF16) {
-    // the bf16 tile goes through LDS (row r of 256 bf16, 16-byte chunk c at
-    // c ^ (r & 15)) so that it leaves in whole rows; the barrier also means
-    // every wave is past its last stage read
+    // the bf16 tile goes through LDS (row r of BN bf16, 16-byte chunk c at
+    // c ^ (r & SWZ): 32 chunks a row at BN = 256, 24 = 3 x 8 at 192) so that
+    // it leaves in whole rows; the barrier also means every wave is past its
+    // last stage read
+    constexpr int RB = 2 * BN, SWZ = BN == 256 ? 15 : 7;
     barrier();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -306,23 +336,24 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
 #pragma unroll
           for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(facc[i][j][g][q]);
           const int chunk = wn * 4 * CI + i * 4 + g;
-          *reinterpret_cast<uint2*>(smem + r * 512 + ((chunk ^ (r & 15)) << 4) + 8 * (lane >> 5)) =
+          *reinterpret_cast<uint2*>(smem + r * RB + ((chunk ^ (r & SWZ)) << 4) + 8 * (lane >> 5)) =
               make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
     }
     waitcnt<63, 0>();
     barrier();
     // wave w stores tile rows RPW w .. RPW w + RPW - 1, two rows per
-    // instruction
-    constexpr int RPW = BM / NWV;
-    const int cl = lane & 31;
+    // instruction (a row is LPR lanes of 8 values; at BN = 192 lanes 48..63
+    // idle)
+    constexpr int RPW = BM / NWV, LPR = BN / 8;
+    const int cl = lane % LPR, rl = lane / LPR;
     const int n = n0 + 8 * cl;
     const bool vec8 = (N & 7) == 0 && n + 7 < N;
 #pragma unroll 4
     for (int it = 0; it < RPW / 2; ++it) {
-      const int r = wave * RPW + 2 * it + (lane >> 5);
-      const v4i v = *reinterpret_cast<const v4i*>(smem + r * 512 + ((cl ^ (r & 15)) << 4));
-      if (r >= mrows || n >= N) continue;
+      const int r = wave * RPW + 2 * it + (rl < 2 ? rl : 1);
+      const v4i v = *reinterpret_cast<const v4i*>(smem + r * RB + ((cl ^ (r & SWZ)) << 4));
+      if (rl >= 2 || r >= mrows || n >= N) continue;
       uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)(m0 + r) * N + n;
       if (vec8) {
         // written once, not read back by this kernel
@@ -352,12 +383,12 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
   }
 }
 
-template <int MODE, int OUT, int NWM, int NWN = 2>
+template <int MODE, int OUT, int NWM, int NWN = 2, int BN = 256>
 void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float* sa, const int8_t* W,
                          const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E,
                          float* qs = nullptr, int clo = 0, int chi = 0x7fffffff) {
-  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM, NWN>), grid, dim3(64 * NWM * NWN), 0, st, A, sa, W, sw, off, Y, M,
-                     N, K, TM, TN, E, qs, clo, chi);
+  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM, NWN, BN>), grid, dim3(64 * NWM * NWN), 0, st, A, sa, W, sw, off, Y,
+                     M, N, K, TM, TN, E, qs, clo, chi);
 }
 
 // Sum of the S fp32 slices' partial tiles, in slice order, then the output.
@@ -458,26 +489,64 @@ hipError_t grouped_launches(const int8_t* A, const float* sa, const int8_t* W, c
 
 }  // namespace
 
+namespace {
+// Tile shape and K split of the dense tile kernels.  128-row tiles for few
+// rows, and where 256-row tiles would leave CUs idle (twice the tiles before
+// any K split: DeepSeek's q_a and kv_a projections at 4096 tokens run
+// 11-14 % faster than on split 256-row tiles); those are 128 x 256 on eight
+// waves as 4 (n) x 2 (m) (two MFMA waves per SIMD: another 4-5 %) or
+// 128 x 192 on four waves, whichever the slice model (pick_k_slices) times
+// lower: 192-wide tiles fill the CUs where 256-wide ones leave some idle
+// (q_a: 256 tiles instead of 192) and leave no ragged tile where N is a
+// multiple of 192 (kv_a, N = 576).
+struct BlockPlan {
+  int BM, BN, TM, TN, S;
+};
+BlockPlan plan_block(int64_t M, int64_t N, int64_t K) {
+  const int KB = (int)(K >> 7);
+  BlockPlan p;
+  p.BN = 256;
+  p.TN = (int)((N + 255) / 256);
+  p.BM = (M <= 128 || ((M + 255) / 256) * p.TN < kTileCUs) ? 128 : 256;
+  p.TM = (int)((M + p.BM - 1) / p.BM);
+  // microseconds per tile and K block, measured at 4096 rows: 2.6 for
+  // 256 x 256 (gate_up), 1.4 for 128 x 256 and 1.26 for 128 x 192 (q_a, one
+  // round of tiles)
+  double t = 0.0;
+  p.S = pick_k_slices((int64_t)p.TM * p.TN, KB, M, N, p.BM == 256 ? 2.6 : 1.4, &t);
+  if (p.BM == 128) {
+    const int TN3 = (int)((N + 191) / 192);
+    double t3 = 0.0;
+    const int S3 = pick_k_slices((int64_t)p.TM * TN3, KB, M, N, 1.26, &t3);
+    if (t3 < t * 0.97) {
+      p.BN = 192;
+      p.TN = TN3;
+      p.S = S3;
+    }
+  }
+  return p;
+}
+}  // namespace
+
 hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y,
                              OutKind out, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (decode_path_takes(M, N, false)) return launch_gemm_block_decode(A, sa, W, sw, Y, out, M, N, K, st);
-  const int TN = (int)((N + 255) / 256);
-  // 128-row tiles for few rows, and where 256-row tiles would leave CUs idle
-  // (twice the tiles before any K split: DeepSeek's q_a and kv_a projections
-  // at 4096 tokens run 11-14 % faster than on split 256-row tiles), on eight
-  // waves as 4 (n) x 2 (m) (two MFMA waves per SIMD: another 4-5 %)
-  const int BM = (M <= 128 || ((M + 255) / 256) * TN < kTileCUs) ? 128 : 256;
-  const int TM = (int)((M + BM - 1) / BM);
-  // ~2.6 us per 256 x 256 tile and K block (1.7 for 128 x 256) at the
-  // measured large-M rate
-  const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, BM == 256 ? 2.6 : 1.7);
+  const BlockPlan p = plan_block(M, N, K);
+  const int BM = p.BM, TM = p.TM, TN = p.TN, S = p.S;
   // a split K takes the stream's scratch, held until the reduction is enqueued
   const WsLease lease = stream_workspace(st, 0, S > 1 ? (size_t)S * M * N * 4 : 0);
   if (lease.status() != kWsOk) return ws_error(lease);
   void* dst = S > 1 ? lease.ptr() : Y;
   const dim3 grid((unsigned)(TM * TN), (unsigned)S);
   const bool f32 = S > 1 || out == OUT_F32;
-  if (BM == 128) {
+  if (p.BN == 192) {
+    if (f32)
+      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 2, 192>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N,
+                                                            (int)K, TM, TN, 0);
+    else
+      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2, 2, 192>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N,
+                                                             (int)K, TM, TN, 0);
+  } else if (BM == 128) {
     if (f32)
       launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K,
                                                        TM, TN, 0);
@@ -516,12 +585,12 @@ hipError_t launch_gemm_block_q8(const int8_t* A, const float* sa, const int8_t* 
     if (e != hipSuccess) return e;
     return launch_quant_group(lease.ptr(), false, M, N, q, qs, st);
   }
-  // the tile kernels, tile height and K split as in launch_gemm_block (the
-  // same kernels, so the same fp32 sums and bf16 values)
+  // the tile kernels with launch_gemm_block's tile height and K split on
+  // 256-wide tiles (a wave's 128 columns are one group): every output is
+  // the same fp32 sum over the same slices, so the same bf16 value
+  const BlockPlan p = plan_block(M, N, K);
   const int TN = (int)((N + 255) / 256);
-  const int BM = (M <= 128 || ((M + 255) / 256) * TN < kTileCUs) ? 128 : 256;
-  const int TM = (int)((M + BM - 1) / BM);
-  const int S = pick_k_slices((int64_t)TM * TN, K >> 7, M, N, BM == 256 ? 2.6 : 1.7);
+  const int BM = p.BM, TM = p.TM, S = p.S;
   const dim3 grid((unsigned)(TM * TN), (unsigned)S);
   if (S == 1) {
     if (BM == 128)

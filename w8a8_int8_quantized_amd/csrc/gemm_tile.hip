@@ -449,7 +449,7 @@ bool stream_capturing(hipStream_t st) {
 // round of workgroups per 256, t_kb microseconds per tile and K block, and
 // splitting adds the slices' partial tiles through HBM (written and read,
 // 8 bytes per output per slice at ~5 TB/s) plus a reduction launch.
-int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us) {
+int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us, double* t_us) {
   int best = 1;
   double best_t = 1e30;
   for (int S = 1; S <= 16 && S <= KB; ++S) {
@@ -461,6 +461,7 @@ int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_u
       best = S;
     }
   }
+  if (t_us) *t_us = best_t;
   return best;
 }
 

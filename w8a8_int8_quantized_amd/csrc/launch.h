@@ -80,8 +80,9 @@ using WsLease = WorkspaceCache<HipScratch>::Lease;
 WsLease stream_workspace(hipStream_t st, int slot, size_t bytes);
 hipError_t ws_error(const WsLease& lease);
 // Number of K slices (1..16) for a grid of `tiles` workgroups over KB K
-// blocks, from a model with t_kb_us microseconds per tile and K block.
-int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us);
+// blocks, from a model with t_kb_us microseconds per tile and K block;
+// t_us, when given, receives the modelled time of the pick.
+int pick_k_slices(int64_t tiles, int64_t KB, int64_t M, int64_t N, double t_kb_us, double* t_us = nullptr);
 
 // Small-M (weight-streaming) variants, used by the dispatchers above for the
 // shapes decode_path_takes accepts: every M <= 64, and channel-wise M <= 128
