@@ -9,7 +9,8 @@
 // Tile: 256 (n) x BM (m), BM = 64 NWM, 2 NWM waves in a 2 (n) x NWM (m) grid,
 // each wave 128 (n) x 64 (m) as 4 x 2 fragments ("chains") of
 // v_mfma_i32_32x32x32_i8 (128-row tiles also come as 256 x 128 on eight
-// waves of 64 x 64 and as 192 x 128 on four waves of 96 x 64); a chain is four MFMAs over one K block (its exact
+// waves of 64 x 64 and as 192 x 128 on eight waves of 96 x 64, four on the
+// even and four on the odd K blocks); a chain is four MFMAs over one K block (its exact
 // int32 P), then 16 cvt + 16 fma per lane dequantise it into the wave's fp32
 // accumulators, which stay in VGPRs.  Operands stream global -> LDS through
 // direct-to-LDS loads into a two-slot ring (pipeline.h), one K block per slot.
@@ -48,8 +49,13 @@ constexpr int kTileCUs = 256;   // compute units the tile grids are sized agains
 // waves of 96 (n) x 64 (m), 3 x 2 chains; a wave's columns may then straddle
 // two 128-column weight-scale blocks, so each 32-column chain takes its own
 // weight scale).
-template <int MODE, int OUT, int NWM, int NWN = 2, int BN = 256>
-__global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
+// KP (with BN = 192): the four waves' sub-tiles are computed twice over, by
+// waves 0..3 on the even K blocks of the slice and by waves 4..7 on the odd
+// ones, each into its own fp32 accumulators, summed (even + odd) at the end;
+// two MFMA waves per SIMD, and four 40 KB stages (two blocks in use, two in
+// flight) fill the 160 KB of LDS.
+template <int MODE, int OUT, int NWM, int NWN = 2, int BN = 256, bool KP = false>
+__global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                              const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                              const int32_t* __restrict__ offsets, void* __restrict__ Y,
                                                              int M, int N, int K, int TM, int TN, int E,
@@ -58,20 +64,25 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
   static_assert(NWN == 2 || (NWN == 4 && OUT != OUT_Q8), "a Q8 group is one wave's 128 columns");
   static_assert(BN == 256 || (BN == 192 && NWM == 2 && NWN == 2 && MODE == MODE_DEQUANT && OUT != OUT_Q8),
                 "192-wide tiles: dense, 128 rows, four waves, bf16 / fp32 output");
-  constexpr int BM = 64 * NWM, NWV = NWN * NWM;
+  static_assert(!KP || BN == 192, "K-block parity: 192-wide tiles (four 40 KB stages)");
+  constexpr int BM = 64 * NWM, NWV = NWN * NWM * (KP ? 2 : 1);   // NWV: waves of the workgroup
+  constexpr int KS = KP ? 2 : 1;      // K-block stride of a wave
+  constexpr int NSTG = 2 * KS;        // LDS stages
   constexpr int CI = BN / (32 * NWN);   // 32-column chains per wave along n
   constexpr int WC = 32 * CI;           // columns per wave
   // weight scales per wave and K block: one where the wave's columns lie in
   // one 128-wide N block, else one per chain
   constexpr int NSW = (128 % WC) == 0 ? 1 : CI;
   constexpr int STG = (BM + BN) * 128;
-  constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A (= 4)
+  constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A
   constexpr int WI = BN / (8 * NWV);   // ... and for W
   constexpr bool DQ = MODE != MODE_PARTIALS;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STG];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTG * STG];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave % NWN, wm = wave / NWN;
+  const int wsub = KP ? (wave & 3) : wave;   // the wave's sub-tile
+  const int par = KP ? (wave >> 2) : 0;      // its first K block (KP: its parity)
+  const int wn = wsub % NWN, wm = wsub / NWN;
   const int KB = K >> 7;
   const int NB = (N + 127) >> 7;
 
@@ -179,7 +190,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
   const bool wact = wm * 64 < mrows;
 #define BK_DMA(T)                                                                                  \
   {                                                                                               \
-    const uint32_t base = lds0 + ((T) & 1) * STG;                                                 \
+    const uint32_t base = lds0 + ((T) & (NSTG - 1)) * STG;                                        \
     _Pragma("unroll") for (int b = 0; b < AI; ++b)                                                \
       if ((wave * AI + b) * 8 < mrows) dma16(ra, voffA, b * K8 + (T) * 128, base + (wave * AI + b) * 1024); \
     _Pragma("unroll") for (int b = 0; b < WI; ++b)                                                \
@@ -189,24 +200,32 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
   // weight-scale index of chain i (i past the last chain: never drained)
 #define QI(i) (NSW == 1 || (i) >= NSW ? 0 : (i))
   const int NK = kbe - kbs;   // K blocks of this slice, numbered from its first
-  // scales of the next block to compute (loaded one block ahead), and the
-  // pending chain: chain 7 (i = 3, j = 1) of the previous block
+  // scales of the wave's next block (loaded one of its blocks ahead), and
+  // the pending chain: the last chain (CI - 1, 1) of the wave's previous block
   float la0 = 0.f, la1 = 0.f, lw[NSW];
 #pragma unroll
   for (int q = 0; q < NSW; ++q) lw[q] = 0.f;
-  if (DQ && NK > 0) {
-    la0 = sa_t[sao[0]];
-    la1 = sa_t[sao[1]];
+  if (DQ && par < NK) {
+    la0 = sa_t[sao[0] + par];
+    la1 = sa_t[sao[1] + par];
 #pragma unroll
-    for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][0];
+    for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][par];
   }
   float sp = 0.f;
   v16i pp = {};
-  if (NK > 0) BK_DMA(0)
-  for (int kb = 0; kb < NK; ++kb) {
-    waitcnt<0, 0>();   // block kb and its scales landed; own reads of kb-1 done
-    barrier();         // everyone's block kb landed; everyone is past kb-1
-    if (kb + 1 < NK) BK_DMA(kb + 1)
+  // iteration it: the blocks KS it .. KS it + KS - 1 are in LDS, the wave
+  // computes block KS it + par
+  const int NIT = (NK + KS - 1) / KS;
+#pragma unroll
+  for (int T = 0; T < KS; ++T)
+    if (T < NK) BK_DMA(T)
+  for (int it = 0; it < NIT; ++it) {
+    const int kb = KS * it + par;
+    waitcnt<0, 0>();   // this iteration's blocks landed; own reads of the last done
+    barrier();         // everyone's landed; everyone is past the last iteration
+#pragma unroll
+    for (int T = 0; T < KS; ++T)
+      if (KS * (it + 1) + T < NK) BK_DMA(KS * (it + 1) + T)
     // scale of chain (i, j): sc0[i] for j = 0, sc1[i] for j = 1 (index 0
     // when the wave has one weight scale)
     float sc0[NSW], sc1[NSW];
@@ -215,15 +234,16 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
       sc0[q] = __fmul_rn(la0, lw[q]);
       sc1[q] = __fmul_rn(la1, lw[q]);
     }
+    if (kb >= NK) continue;   // KP: no odd block in the last iteration
     if (DQ) {
-      const int kn = kb + 1 < NK ? kb + 1 : kb;
+      const int kn = kb + KS < NK ? kb + KS : kb;
       la0 = sa_t[sao[0] + kn];
       la1 = sa_t[sao[1] + kn];
 #pragma unroll
       for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][kn];
     }
     if (!wact) continue;
-    const char* buf = smem + (kb & 1) * STG;
+    const char* buf = smem + (kb & (NSTG - 1)) * STG;
     v4i af[2][4], wc[4], wnx[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -244,7 +264,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_i32_32x32x32_i8(wc[ks], af[j][ks], c, 0, 0, 0);
       if (t == 0) {
-        if (kb > 0) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, kb - 1);
+        if (it > 0) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, kb - KS);
       } else if (t & 1) {   // previous chain: (i, 0)
         if (i == 0) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, sc0[0], kb);
         if (i == 1) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sc0[QI(1)], kb);
@@ -274,9 +294,40 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
   }
 #undef BK_DMA
 #undef QI
-  if (NK > 0 && wact) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, NK - 1);
+  // the wave's last block: the last of its parity
+  if (par < NK && wact)
+    drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp,
+          NK - 1 - ((NK - 1 - par) % KS));
   waitcnt<0, 0>();
   if (!DQ) return;
+  if constexpr (KP) {
+    // odd-block sums through LDS (every wave is past its stage reads after
+    // the barrier), added to the even-block sums in fixed order: even + odd
+    constexpr int NV = CI * 2 * 4;   // v4f accumulators per lane
+    v4f* red = reinterpret_cast<v4f*>(smem) + wsub * NV * 64 + lane;
+    barrier();
+    if (par == 1) {
+#pragma unroll
+      for (int i = 0; i < CI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) red[((i * 2 + j) * 4 + g) * 64] = facc[i][j][g];
+    }
+    wait_barrier<63, 0>();
+    if (par == 0) {
+#pragma unroll
+      for (int i = 0; i < CI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v4f o = red[((i * 2 + j) * 4 + g) * 64];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) facc[i][j][g][r] = __fadd_rn(facc[i][j][g][r], o[r]);
+          }
+    }
+  }
 
   if (OUT == OUT_Q8) {
     // The 128 columns of this wave are one quantisation group of the next
@@ -327,6 +378,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
     barrier();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      if (par != 0) break;   // KP: the even waves hold the sums
       const int r = wm * 64 + j * 32 + (lane & 31);
 #pragma unroll
       for (int i = 0; i < CI; ++i)
@@ -366,6 +418,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
     }
     return;
   }
+  if (par != 0) return;   // KP: the even waves hold the sums
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ml = wm * 64 + j * 32 + (lane & 31);
@@ -383,12 +436,12 @@ __global__ __launch_bounds__(64 * NWM * NWN, 1) void k_gemm_block(const int8_t* 
   }
 }
 
-template <int MODE, int OUT, int NWM, int NWN = 2, int BN = 256>
+template <int MODE, int OUT, int NWM, int NWN = 2, int BN = 256, bool KP = false>
 void launch_block_kernel(dim3 grid, hipStream_t st, const int8_t* A, const float* sa, const int8_t* W,
                          const float* sw, const int32_t* off, void* Y, int M, int N, int K, int TM, int TN, int E,
                          float* qs = nullptr, int clo = 0, int chi = 0x7fffffff) {
-  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM, NWN, BN>), grid, dim3(64 * NWM * NWN), 0, st, A, sa, W, sw, off, Y,
-                     M, N, K, TM, TN, E, qs, clo, chi);
+  hipLaunchKernelGGL((k_gemm_block<MODE, OUT, NWM, NWN, BN, KP>), grid, dim3(64 * NWM * NWN * (KP ? 2 : 1)), 0, st, A,
+                     sa, W, sw, off, Y, M, N, K, TM, TN, E, qs, clo, chi);
 }
 
 // Sum of the S fp32 slices' partial tiles, in slice order, then the output.
@@ -495,10 +548,10 @@ namespace {
 // any K split: DeepSeek's q_a and kv_a projections at 4096 tokens run
 // 11-14 % faster than on split 256-row tiles); those are 128 x 256 on eight
 // waves as 4 (n) x 2 (m) (two MFMA waves per SIMD: another 4-5 %) or
-// 128 x 192 on four waves, whichever the slice model (pick_k_slices) times
-// lower: 192-wide tiles fill the CUs where 256-wide ones leave some idle
-// (q_a: 256 tiles instead of 192) and leave no ragged tile where N is a
-// multiple of 192 (kv_a, N = 576).
+// 128 x 192 on eight waves by K-block parity, whichever the slice model
+// (pick_k_slices) times lower: 192-wide tiles fill the CUs where 256-wide
+// ones leave some idle (q_a: 256 tiles instead of 192) and leave no ragged
+// tile where N is a multiple of 192 (kv_a, N = 576).
 struct BlockPlan {
   int BM, BN, TM, TN, S;
 };
@@ -510,14 +563,14 @@ BlockPlan plan_block(int64_t M, int64_t N, int64_t K) {
   p.BM = (M <= 128 || ((M + 255) / 256) * p.TN < kTileCUs) ? 128 : 256;
   p.TM = (int)((M + p.BM - 1) / p.BM);
   // microseconds per tile and K block, measured at 4096 rows: 2.6 for
-  // 256 x 256 (gate_up), 1.4 for 128 x 256 and 1.26 for 128 x 192 (q_a, one
-  // round of tiles)
+  // 256 x 256 (gate_up), 1.4 for 128 x 256 and 1.17 for the K-parity
+  // 128 x 192 tiles (q_a, one round of tiles)
   double t = 0.0;
   p.S = pick_k_slices((int64_t)p.TM * p.TN, KB, M, N, p.BM == 256 ? 2.6 : 1.4, &t);
   if (p.BM == 128) {
     const int TN3 = (int)((N + 191) / 192);
     double t3 = 0.0;
-    const int S3 = pick_k_slices((int64_t)p.TM * TN3, KB, M, N, 1.26, &t3);
+    const int S3 = pick_k_slices((int64_t)p.TM * TN3, KB, M, N, 1.17, &t3);
     if (t3 < t * 0.97) {
       p.BN = 192;
       p.TN = TN3;
@@ -541,11 +594,11 @@ hipError_t launch_gemm_block(const int8_t* A, const float* sa, const int8_t* W, 
   const bool f32 = S > 1 || out == OUT_F32;
   if (p.BN == 192) {
     if (f32)
-      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 2, 192>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N,
-                                                            (int)K, TM, TN, 0);
+      launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 2, 192, true>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N,
+                                                                  (int)K, TM, TN, 0);
     else
-      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2, 2, 192>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N,
-                                                             (int)K, TM, TN, 0);
+      launch_block_kernel<MODE_DEQUANT, OUT_BF16, 2, 2, 192, true>(grid, st, A, sa, W, sw, nullptr, dst, (int)M,
+                                                                   (int)N, (int)K, TM, TN, 0);
   } else if (BM == 128) {
     if (f32)
       launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 4>(grid, st, A, sa, W, sw, nullptr, dst, (int)M, (int)N, (int)K,
@@ -587,8 +640,22 @@ hipError_t launch_gemm_block_q8(const int8_t* A, const float* sa, const int8_t* 
   }
   // the tile kernels with launch_gemm_block's tile height and K split on
   // 256-wide tiles (a wave's 128 columns are one group): every output is
-  // the same fp32 sum over the same slices, so the same bf16 value
+  // the same fp32 sum over the same slices, so the same bf16 value.  Where
+  // launch_gemm_block takes the K-parity 192-wide tiles (whose sums add the
+  // odd blocks' sum to the even blocks'), the same kernel writes fp32 slices
+  // and the slice-sum kernel quantises them.
   const BlockPlan p = plan_block(M, N, K);
+  if (p.BN == 192) {
+    const WsLease lease = stream_workspace(st, 0, (size_t)p.S * M * N * 4);
+    if (lease.status() != kWsOk) return ws_error(lease);
+    launch_block_kernel<MODE_DEQUANT, OUT_F32, 2, 2, 192, true>(dim3((unsigned)(p.TM * p.TN), (unsigned)p.S), st, A,
+                                                                sa, W, sw, nullptr, lease.ptr(), (int)M, (int)N,
+                                                                (int)K, p.TM, p.TN, 0);
+    const dim3 rg((unsigned)((M * (N / 4) + 255) / 256));
+    hipLaunchKernelGGL(k_splitk_sum_f32_q8, rg, dim3(256), 0, st, static_cast<const float*>(lease.ptr()), p.S, (int)M,
+                       (int)N, q, qs);
+    return hipGetLastError();
+  }
   const int TN = (int)((N + 255) / 256);
   const int BM = p.BM, TM = p.TM, S = p.S;
   const dim3 grid((unsigned)(TM * TN), (unsigned)S);
