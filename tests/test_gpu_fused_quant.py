@@ -52,10 +52,13 @@ def _check_against_composition(q, s, ybf16, rows=None):
     assert np.array_equal(sn.view(np.uint32), os_.view(np.uint32))
 
 
-# (M, N, K): a 2048 x 8192 grid of 256-row tiles runs unsplit; 300 rows and
-# 24 rows take 128-row tiles with K split; 1 and 64 rows are decode-sized.
-@pytest.mark.parametrize("M,N,K", [(2048, 8192, 1024), (300, 1024, 1024), (24, 1536, 2048), (1, 4096, 1024),
-                                   (64, 12288, 4096), (513, 384, 640)])
+# (M, N, K): a 2048 x 8192 grid of 256-row tiles runs unsplit; 1500 x 5120
+# takes 128 x 256 tiles unsplit (the quantising epilogue) and 513 x 384 split
+# over K (slices quantised in the sum); 300 x 1024 is where gemm_w8a8_block
+# takes the K-parity 128 x 192 tiles, split over K, whose fp32 slices the
+# quantising call sums; 1, 24 and 64 rows are decode-sized.
+@pytest.mark.parametrize("M,N,K", [(2048, 8192, 1024), (1500, 5120, 256), (300, 1024, 1024), (24, 1536, 2048),
+                                   (1, 4096, 1024), (64, 12288, 4096), (513, 384, 640)])
 def test_block_quant_equals_gemm_then_group_quant(M, N, K):
     qa, sa, qw, sw = _block_operands(M, N, K, seed=M + N)
     A, SA, W, SW = (torch.from_numpy(a).to(DEV) for a in (qa, sa, qw, sw))
