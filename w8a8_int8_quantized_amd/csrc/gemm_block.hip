@@ -188,6 +188,7 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
   // feed only outputs that are never stored), and a wave whose 64 rows all
   // lie past them skips its MFMAs (MoE expert tiles are often part-empty)
   const bool wact = wm * 64 < mrows;
+  const bool half = wm * 64 + 32 >= mrows;   // (with wact) only the first fragment has rows
 #define BK_DMA(T)                                                                                  \
   {                                                                                               \
     const uint32_t base = lds0 + ((T) & (NSTG - 1)) * STG;                                        \
@@ -213,49 +214,25 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
   }
   float sp = 0.f;
   v16i pp = {};
-  // iteration it: the blocks KS it .. KS it + KS - 1 are in LDS, the wave
-  // computes block KS it + par
-  const int NIT = (NK + KS - 1) / KS;
+  // One K block's chains from LDS buffer buf, JM 32-row fragments per wave
+  // (JM = 1: the wave's second fragment lies wholly past the tile's rows, so
+  // its MFMAs and dequantisation are skipped).  Chain t = JM i + j;
+  // its MFMAs run interleaved with the dequantisation of chain t - 1 (at
+  // t = 0, the wave's previous block's last chain).
+  auto block_chains = [&](auto jmc, const char* buf, int kb, int it, const float* sc0, const float* sc1) {
+    constexpr int JM = decltype(jmc)::value;
+    v4i af[JM][4], wc[4], wnx[4];
 #pragma unroll
-  for (int T = 0; T < KS; ++T)
-    if (T < NK) BK_DMA(T)
-  for (int it = 0; it < NIT; ++it) {
-    const int kb = KS * it + par;
-    waitcnt<0, 0>();   // this iteration's blocks landed; own reads of the last done
-    barrier();         // everyone's landed; everyone is past the last iteration
-#pragma unroll
-    for (int T = 0; T < KS; ++T)
-      if (KS * (it + 1) + T < NK) BK_DMA(KS * (it + 1) + T)
-    // scale of chain (i, j): sc0[i] for j = 0, sc1[i] for j = 1 (index 0
-    // when the wave has one weight scale)
-    float sc0[NSW], sc1[NSW];
-#pragma unroll
-    for (int q = 0; q < NSW; ++q) {
-      sc0[q] = __fmul_rn(la0, lw[q]);
-      sc1[q] = __fmul_rn(la1, lw[q]);
-    }
-    if (kb >= NK) continue;   // KP: no odd block in the last iteration
-    if (DQ) {
-      const int kn = kb + KS < NK ? kb + KS : kb;
-      la0 = sa_t[sao[0] + kn];
-      la1 = sa_t[sao[1] + kn];
-#pragma unroll
-      for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][kn];
-    }
-    if (!wact) continue;
-    const char* buf = smem + (kb & (NSTG - 1)) * STG;
-    v4i af[2][4], wc[4], wnx[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JM; ++j)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) af[j][ks] = *(const v4i*)(buf + (wm * 64 + j * 32) * 128 + lo[ks]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) wc[ks] = *(const v4i*)(buf + BM * 128 + (wn * WC) * 128 + lo[ks]);
-    // chain t = 2 i + j
 #pragma unroll
-    for (int t = 0; t < 2 * CI; ++t) {
-      const int i = t >> 1, j = t & 1;
-      if (j == 0 && i < CI - 1) {
+    for (int t = 0; t < JM * CI; ++t) {
+      const int i = t / JM, j = t % JM;
+      const bool rd = j == 0 && i < CI - 1;   // the next chain's W fragments are read now
+      if (rd) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           wnx[ks] = *(const v4i*)(buf + BM * 128 + (wn * WC + (i + 1) * 32) * 128 + lo[ks]);
@@ -264,40 +241,88 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_i32_32x32x32_i8(wc[ks], af[j][ks], c, 0, 0, 0);
       if (t == 0) {
-        if (it > 0) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp, kb - KS);
-      } else if (t & 1) {   // previous chain: (i, 0)
-        if (i == 0) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, sc0[0], kb);
-        if (i == 1) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, sc0[QI(1)], kb);
-        if (i == 2) drain(pp, std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{}, sc0[QI(2)], kb);
-        if (i == 3) drain(pp, std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{}, sc0[QI(3)], kb);
-      } else {              // previous chain: (i - 1, 1)
-        if (i == 1) drain(pp, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, sc1[0], kb);
-        if (i == 2) drain(pp, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, sc1[QI(1)], kb);
-        if (i == 3) drain(pp, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}, sc1[QI(2)], kb);
+        if (it > 0)
+          drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, JM - 1>{}, sp, kb - KS);
+      } else {
+        // previous chain (ip, jp), tp = t - 1 = JM ip + jp
+        const int tp = t - 1;
+#define BK_DRAIN(IP, JP)                                                                                     \
+  if (JP < JM && tp == IP * JM + JP)                                                                         \
+    drain(pp, std::integral_constant<int, IP>{}, std::integral_constant<int, JP>{}, (JP == 0 ? sc0 : sc1)[QI(IP)], kb);
+        BK_DRAIN(0, 0) BK_DRAIN(0, 1) BK_DRAIN(1, 0) BK_DRAIN(1, 1)
+        BK_DRAIN(2, 0) BK_DRAIN(2, 1) BK_DRAIN(3, 0)
+#undef BK_DRAIN
       }
-      // one MFMA, then eight VALU ops, four times; the next pair's W reads
+      // one MFMA, then eight VALU ops, four times; the next chain's W reads
       // ride along
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        if (j == 0 && i < CI - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       pp = c;
-      if (j == 1 && i < CI - 1) {
+      if (j == JM - 1 && i < CI - 1) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) wc[ks] = wnx[ks];
       }
     }
-    sp = sc1[QI(CI - 1)];
+    sp = (JM == 2 ? sc1 : sc0)[QI(CI - 1)];
+  };
+  // The K loop, JM fragments per wave throughout.  Iteration it: the blocks
+  // KS it .. KS it + KS - 1 are in LDS, the wave computes block KS it + par.
+  auto kloop = [&](auto jmc) {
+    constexpr int JM = decltype(jmc)::value;
+    const int NIT = (NK + KS - 1) / KS;
+#pragma unroll
+    for (int T = 0; T < KS; ++T)
+      if (T < NK) BK_DMA(T)
+    for (int it = 0; it < NIT; ++it) {
+      const int kb = KS * it + par;
+      waitcnt<0, 0>();   // this iteration's blocks landed; own reads of the last done
+      barrier();         // everyone's landed; everyone is past the last iteration
+#pragma unroll
+      for (int T = 0; T < KS; ++T)
+        if (KS * (it + 1) + T < NK) BK_DMA(KS * (it + 1) + T)
+      // scale of chain (i, j): sc0[i] for j = 0, sc1[i] for j = 1 (index 0
+      // when the wave has one weight scale)
+      float sc0[NSW], sc1[NSW];
+#pragma unroll
+      for (int q = 0; q < NSW; ++q) {
+        sc0[q] = __fmul_rn(la0, lw[q]);
+        sc1[q] = __fmul_rn(la1, lw[q]);
+      }
+      if (kb >= NK) continue;   // KP: no odd block in the last iteration
+      if (DQ) {
+        const int kn = kb + KS < NK ? kb + KS : kb;
+        la0 = sa_t[sao[0] + kn];
+        la1 = sa_t[sao[1] + kn];
+#pragma unroll
+        for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][kn];
+      }
+      if (!wact) continue;
+      block_chains(jmc, smem + (kb & (NSTG - 1)) * STG, kb, it, sc0, sc1);
+    }
+    // the wave's last block: the last of its parity
+    if (par < NK && wact)
+      drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, JM - 1>{}, sp,
+            NK - 1 - ((NK - 1 - par) % KS));
+  };
+  // Waves whose second fragment has no rows run a K loop of their own
+  // (a branch inside the loop would tie both forms to one register
+  // assignment); only the grouped 256-row tiles, where MoE experts of
+  // 129-160 rows leave such a wave beside a full one on a SIMD, have it.
+  if constexpr (MODE == MODE_GROUPED && NWM == 4) {
+    if (half)
+      kloop(std::integral_constant<int, 1>{});
+    else
+      kloop(std::integral_constant<int, 2>{});
+  } else {
+    kloop(std::integral_constant<int, 2>{});
   }
 #undef BK_DMA
 #undef QI
-  // the wave's last block: the last of its parity
-  if (par < NK && wact)
-    drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, 1>{}, sp,
-          NK - 1 - ((NK - 1 - par) % KS));
   waitcnt<0, 0>();
   if (!DQ) return;
   if constexpr (KP) {
