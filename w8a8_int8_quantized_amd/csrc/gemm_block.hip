@@ -188,7 +188,6 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
   // feed only outputs that are never stored), and a wave whose 64 rows all
   // lie past them skips its MFMAs (MoE expert tiles are often part-empty)
   const bool wact = wm * 64 < mrows;
-  const bool half = wm * 64 + 32 >= mrows;   // (with wact) only the first fragment has rows
 #define BK_DMA(T)                                                                                  \
   {                                                                                               \
     const uint32_t base = lds0 + ((T) & (NSTG - 1)) * STG;                                        \
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
   // assignment); only the grouped 256-row tiles, where MoE experts of
   // 129-160 rows leave such a wave beside a full one on a SIMD, have it.
   if constexpr (MODE == MODE_GROUPED && NWM == 4) {
-    if (half)
+    if (wm * 64 + 32 >= mrows)   // (with wact) only the first fragment has rows
       kloop(std::integral_constant<int, 1>{});
     else
       kloop(std::integral_constant<int, 2>{});
