@@ -77,7 +77,13 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
   constexpr int AI = BM / (8 * NWV);   // DMA instructions per wave per K block for A
   constexpr int WI = BN / (8 * NWV);   // ... and for W
   constexpr bool DQ = MODE != MODE_PARTIALS;
-  __shared__ __attribute__((aligned(1024))) char smem[NSTG * STG];
+  // activation scales staged in LDS (not with KP, whose stages fill it):
+  // 16 K blocks of every tile row (64 bytes a row) per chunk, two chunks
+  constexpr bool SCL = DQ && !KP;
+  constexpr int SCB = SCL ? BM * 64 : 0;   // bytes of one scale chunk
+  constexpr int SCI = SCL ? BM / (16 * NWV) : 0;   // DMA instructions per wave per chunk
+  static_assert(!SCL || SCI * 16 * NWV == BM, "scale chunk rows split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[NSTG * STG + 2 * SCB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wsub = KP ? (wave & 3) : wave;   // the wave's sub-tile
@@ -146,8 +152,32 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = wm * 64 + j * 32 + (lane & 31);
-    sao[j] = (r < mrows ? r : mrows - 1) * KB;
+    // SCL: the row's offset in a chunk (16-row groups of 1 KB, inside one
+    // four 256-byte pieces of 16 rows x 16 bytes)
+    sao[j] = SCL ? (r >> 4) * 1024 + (r & 15) * 16 : (r < mrows ? r : mrows - 1) * KB;
   }
+  // Scale chunk c (slice blocks 16 c .. 16 c + 15) goes to buffer c % 2 by
+  // direct-to-LDS loads of 16 bytes (four K blocks of one row) per lane, 16
+  // rows per instruction, lane l taking row l % 16 and blocks 4 (l / 16) ..
+  // 4 (l / 16) + 3, so that one block's scales of 16 consecutive rows lie
+  // 16 bytes apart (reads of 32 rows: two-way bank conflicts, not
+  // eight-way); rows past the tile, and bytes past the last row, read zero
+  // through the descriptor (the values past a row's last K block are never
+  // used).  A per-lane load of one scale per K block would touch a cache
+  // line per row.
+  const v4i rsa = make_rsrc(SCL ? sa + (int64_t)m0 * KB : sa, SCL ? (uint32_t)(mrows * KB * 4) : 0u);
+  const uint32_t scl0 = lds_addr(smem) + NSTG * STG;
+#define BK_SCL(C)                                                                                   \
+  _Pragma("unroll") for (int s_ = 0; s_ < SCI; ++s_) {                                             \
+    const int i_ = wave * SCI + s_;                                                                \
+    dma16(rsa, (16 * i_ + (lane & 15)) * KB * 4 + (lane >> 4) * 16, (kbs + 16 * (C)) * 4,          \
+          scl0 + ((C) & 1) * SCB + i_ * 1024);                                                     \
+  }
+  // the activation scale of row offset o (sao) and slice block k, staged
+  auto la_lds = [&](int o, int k) {
+    return *reinterpret_cast<const float*>(smem + NSTG * STG + ((k >> 4) & 1) * SCB + o + ((k >> 2) & 3) * 256 +
+                                           (k & 3) * 4);
+  };
 
   v4f facc[CI][2][4];
 #pragma unroll
@@ -205,7 +235,18 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
   float la0 = 0.f, la1 = 0.f, lw[NSW];
 #pragma unroll
   for (int q = 0; q < NSW; ++q) lw[q] = 0.f;
-  if (DQ && par < NK) {
+  if constexpr (SCL) {
+    if (NK > 0) {
+      // the first chunk, read below after a wait and a barrier of its own
+      BK_SCL(0)
+      waitcnt<0, 0>();
+      barrier();
+      la0 = la_lds(sao[0], 0);
+      la1 = la_lds(sao[1], 0);
+#pragma unroll
+      for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][0];
+    }
+  } else if (DQ && par < NK) {
     la0 = sa_t[sao[0] + par];
     la1 = sa_t[sao[1] + par];
 #pragma unroll
@@ -284,6 +325,10 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
 #pragma unroll
       for (int T = 0; T < KS; ++T)
         if (KS * (it + 1) + T < NK) BK_DMA(KS * (it + 1) + T)
+      // the next scale chunk, into the buffer the previous one used (every
+      // wave is past its reads of it)
+      if constexpr (SCL)
+        if ((it & 15) == 0 && it + 16 < NK) BK_SCL((it >> 4) + 1)
       // scale of chain (i, j): sc0[i] for j = 0, sc1[i] for j = 1 (index 0
       // when the wave has one weight scale)
       float sc0[NSW], sc1[NSW];
@@ -295,8 +340,13 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
       if (kb >= NK) continue;   // KP: no odd block in the last iteration
       if (DQ) {
         const int kn = kb + KS < NK ? kb + KS : kb;
-        la0 = sa_t[sao[0] + kn];
-        la1 = sa_t[sao[1] + kn];
+        if constexpr (SCL) {
+          la0 = la_lds(sao[0], kn);
+          la1 = la_lds(sao[1], kn);
+        } else {
+          la0 = sa_t[sao[0] + kn];
+          la1 = sa_t[sao[1] + kn];
+        }
 #pragma unroll
         for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][kn];
       }
@@ -321,6 +371,7 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
     kloop(std::integral_constant<int, 2>{});
   }
 #undef BK_DMA
+#undef BK_SCL
 #undef QI
   waitcnt<0, 0>();
   if (!DQ) return;
