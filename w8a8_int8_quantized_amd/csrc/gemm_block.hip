@@ -147,14 +147,14 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
     nbw = nbw < NB ? nbw : NB - 1;
     sw_row[q] = swx + (int64_t)nbw * KB + kbs;
   }
-  const float* sa_t = sa + (int64_t)m0 * KB + kbs;   // uniform base, 32-bit lane offsets
   int sao[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = wm * 64 + j * 32 + (lane & 31);
-    // SCL: the row's offset in a chunk (16-row groups of 1 KB, inside one
-    // four 256-byte pieces of 16 rows x 16 bytes)
-    sao[j] = SCL ? (r >> 4) * 1024 + (r & 15) * 16 : (r < mrows ? r : mrows - 1) * KB;
+    // staged (SCL): the row's offset in a chunk (16-row groups of 1 KB,
+    // inside one four 256-byte pieces of 16 rows x 16 bytes); KP: the byte
+    // offset of its slice's first scale
+    sao[j] = SCL ? (r >> 4) * 1024 + (r & 15) * 16 : (r * KB + kbs) * 4;
   }
   // Scale chunk c (slice blocks 16 c .. 16 c + 15) goes to buffer c % 2 by
   // direct-to-LDS loads of 16 bytes (four K blocks of one row) per lane, 16
@@ -173,6 +173,14 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
     dma16(rsa, (16 * i_ + (lane & 15)) * KB * 4 + (lane >> 4) * 16, (kbs + 16 * (C)) * 4,          \
           scl0 + ((C) & 1) * SCB + i_ * 1024);                                                     \
   }
+  // KP: a lane's row's scales of four consecutive K blocks, loaded at once
+  // through a descriptor over the tile's rows (rows past them, and bytes past
+  // the last row, read zero), kept for the wave's next two blocks
+  const __amdgpu_buffer_rsrc_t rsa4 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(KP ? sa + (int64_t)m0 * KB : sa), 0, __builtin_amdgcn_readfirstlane(KP ? mrows * KB * 4 : 0),
+      0x00020000);
+  v4f la4[2] = {};
+  int cb = -8;   // la4 holds slice blocks cb .. cb + 3
   // the activation scale of row offset o (sao) and slice block k, staged
   auto la_lds = [&](int o, int k) {
     return *reinterpret_cast<const float*>(smem + NSTG * STG + ((k >> 4) & 1) * SCB + o + ((k >> 2) & 3) * 256 +
@@ -235,6 +243,16 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
   float la0 = 0.f, la1 = 0.f, lw[NSW];
 #pragma unroll
   for (int q = 0; q < NSW; ++q) lw[q] = 0.f;
+  auto la_kp = [&](int kn) {
+    if (kn - cb >= 4 || kn < cb) {
+      cb = kn;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        la4[j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsa4, sao[j] + kn * 4, 0, 0));
+    }
+    la0 = la4[0][kn - cb];
+    la1 = la4[1][kn - cb];
+  };
   if constexpr (SCL) {
     if (NK > 0) {
       // the first chunk, read below after a wait and a barrier of its own
@@ -246,9 +264,8 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
 #pragma unroll
       for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][0];
     }
-  } else if (DQ && par < NK) {
-    la0 = sa_t[sao[0] + par];
-    la1 = sa_t[sao[1] + par];
+  } else if (KP && par < NK) {
+    la_kp(par);
 #pragma unroll
     for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][par];
   }
@@ -344,8 +361,7 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
           la0 = la_lds(sao[0], kn);
           la1 = la_lds(sao[1], kn);
         } else {
-          la0 = sa_t[sao[0] + kn];
-          la1 = sa_t[sao[1] + kn];
+          la_kp(kn);
         }
 #pragma unroll
         for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][kn];
