@@ -9,11 +9,14 @@
 // Tile: 256 (n) x BM (m), BM = 64 NWM, 2 NWM waves in a 2 (n) x NWM (m) grid,
 // each wave 128 (n) x 64 (m) as 4 x 2 fragments ("chains") of
 // v_mfma_i32_32x32x32_i8 (128-row tiles also come as 256 x 128 on eight
-// waves of 64 x 64 and as 192 x 128 on eight waves of 96 x 64, four on the
-// even and four on the odd K blocks); a chain is four MFMAs over one K block (its exact
-// int32 P), then 16 cvt + 16 fma per lane dequantise it into the wave's fp32
-// accumulators, which stay in VGPRs.  Operands stream global -> LDS through
-// direct-to-LDS loads into a two-slot ring (pipeline.h), one K block per slot.
+// waves of 64 x 64, and as 192 x 128 on eight waves of 96 x 64, four on the
+// even and four on the odd K blocks); a chain is four MFMAs over one K block
+// (its exact int32 P), then 16 cvt + 16 fma per lane dequantise it into the
+// wave's fp32 accumulators, which stay in VGPRs.  Operands stream global ->
+// LDS through direct-to-LDS loads into a two-slot ring (pipeline.h; four
+// slots with K parity), one K block per slot; the activation scales are
+// staged in LDS 16 K blocks at a time, or with K parity loaded four K blocks
+// per lane.
 //
 // Software pipeline: the MFMAs of chain t run interleaved with the
 // dequantisation of chain t - 1 (one MFMA, then eight VALU ops, pinned with
@@ -45,8 +48,8 @@ constexpr int kTileCUs = 256;   // compute units the tile grids are sized agains
 // NWM = 2): a 128 x 256 tile on eight waves, each 64 (n) x 64 (m), 2 x 2
 // chains, so that 128-row tiles keep two MFMA waves per SIMD (bf16 / fp32
 // output: a wave's 64 columns are half a quantisation group).
-// BN: tile width, 256 or 192 (with NWM = NWN = 2: a 128 x 192 tile on four
-// waves of 96 (n) x 64 (m), 3 x 2 chains; a wave's columns may then straddle
+// BN: tile width, 256 or 192 (with NWM = NWN = 2: a 128 x 192 tile of four
+// sub-tiles of 96 (n) x 64 (m), 3 x 2 chains; a wave's columns may straddle
 // two 128-column weight-scale blocks, so each 32-column chain takes its own
 // weight scale).
 // KP (with BN = 192): the four waves' sub-tiles are computed twice over, by
@@ -55,12 +58,10 @@ constexpr int kTileCUs = 256;   // compute units the tile grids are sized agains
 // two MFMA waves per SIMD, and four 40 KB stages (two blocks in use, two in
 // flight) fill the 160 KB of LDS.
 template <int MODE, int OUT, int NWM, int NWN = 2, int BN = 256, bool KP = false>
-__global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block(const int8_t* __restrict__ A, const float* __restrict__ sa,
-                                                             const int8_t* __restrict__ W, const float* __restrict__ sw,
-                                                             const int32_t* __restrict__ offsets, void* __restrict__ Y,
-                                                             int M, int N, int K, int TM, int TN, int E,
-                                                             float* __restrict__ qs = nullptr, int clo = 0,
-                                                             int chi = 0x7fffffff) {
+__global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block(
+    const int8_t* __restrict__ A, const float* __restrict__ sa, const int8_t* __restrict__ W,
+    const float* __restrict__ sw, const int32_t* __restrict__ offsets, void* __restrict__ Y, int M, int N, int K,
+    int TM, int TN, int E, float* __restrict__ qs = nullptr, int clo = 0, int chi = 0x7fffffff) {
   static_assert(NWN == 2 || (NWN == 4 && OUT != OUT_Q8), "a Q8 group is one wave's 128 columns");
   static_assert(BN == 256 || (BN == 192 && NWM == 2 && NWN == 2 && MODE == MODE_DEQUANT && OUT != OUT_Q8),
                 "192-wide tiles: dense, 128 rows, four waves, bf16 / fp32 output");
@@ -151,9 +152,9 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = wm * 64 + j * 32 + (lane & 31);
-    // staged (SCL): the row's offset in a chunk (16-row groups of 1 KB,
-    // inside one four 256-byte pieces of 16 rows x 16 bytes); KP: the byte
-    // offset of its slice's first scale
+    // staged (SCL): the row's offset in a chunk (16-row groups of 1 KB, each
+    // four 256-byte pieces of 16 rows x 16 bytes); KP: the byte offset of its
+    // slice's first scale
     sao[j] = SCL ? (r >> 4) * 1024 + (r & 15) * 16 : (r * KB + kbs) * 4;
   }
   // Scale chunk c (slice blocks 16 c .. 16 c + 15) goes to buffer c % 2 by
