@@ -209,8 +209,10 @@ int gemm_w8a8_channel_noalloc(const int8_t* A, const float* a_scale,
  *   A, a_scale, W, w_scale as gemm_w8a8_block; N % 128 == 0 (W8_ERR_SHAPE
  *   otherwise); q [M][N] int8 out, q_scale [M][N/128] fp32 out.
  * The quantisation runs in the tile kernel's epilogue, or, for small tile
- * grids, in the pass that sums the K slices (split-K workspace as for
- * gemm_w8a8_block).  For decode-sized M (the weight-streaming kernels of
+ * grids and where gemm_w8a8_block takes its 128 x 192 tiles (whose fp32
+ * sums add the odd K blocks' sum to the even ones'), in the pass that sums
+ * the fp32 K slices (one slice or more, in the split-K workspace as for
+ * gemm_w8a8_block, S x M x N x 4 bytes).  For decode-sized M (the weight-streaming kernels of
  * gemm_w8a8_block, whose waves own 16-column slices of a group) the bf16
  * output goes through the same per-stream scratch (M x N x 2 bytes) to the
  * group quantiser: nothing is saved there, but the result is the same.
