@@ -751,15 +751,36 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
     for (int i = 0; i < AG; ++i)
       if (xpos[i] >= 0) xs[buf][xpos[i]] = xreg[i];
   };
+  // The ring holds consecutive K blocks, slot p block it PF + p.  Slots
+  // SB i .. SB i + SB - 1 (SB = 4, or PF if less) share the scales sv[i] of
+  // their SB blocks for the lane's four columns, 4 SB bytes per column,
+  // loaded with the last of those slots (when all of their previous blocks
+  // are done); scales past the slice's last block belong to the next row or
+  // read zero, and multiply weights that read zero.
+  constexpr int SB = PF < 4 ? PF : 4;
+  static_assert(PF % SB == 0 && (SB == 4 || SB == 2), "scales load two or four K blocks at a time");
   typename WF::T wv[PF][2];
-  float sv[PF][4];
+  float sv[PF / SB][4][SB];
   auto load_w = [&](int P, int kb) {
     const uint32_t ko = kb < KB ? (uint32_t)kb * WF::kBytesPerGroup : kOob;
-    const uint32_t so = kb < KB ? (uint32_t)kb * 4u : kOob;
     wv[P][0] = WF::load(rw, woff + ko);
     wv[P][1] = WF::load(rw, woff + ko + WF::kBytesPerGroup / 2);
+    if (P % SB == SB - 1) {
+      const int kf = kb - (SB - 1);   // the first block of the group
+      const uint32_t so = kf < KB ? (uint32_t)kf * 4u : kOob;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[P][r] = blf(rs, soff + r * KBt * 4 + so);
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (SB == 4) {
+          const v4f t = __builtin_bit_cast(v4f, bl16(rs, soff + r * KBt * 4 + so));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[P / SB][r][e] = t[e];
+        } else {
+          const v2i t = bl8(rs, soff + r * KBt * 4 + so);
+          sv[P / SB][r][0] = __builtin_bit_cast(float, t[0]);
+          sv[P / SB][r][1] = __builtin_bit_cast(float, t[1]);
+        }
+      }
+    }
   };
 
   load_act(0);
@@ -796,7 +817,7 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
           pp = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[t], xv, pp, 0, 0, 0);
         }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) facc[j][rr] = __builtin_fmaf(sv[p][rr], pp[rr], facc[j][rr]);
+        for (int rr = 0; rr < 4; ++rr) facc[j][rr] = __builtin_fmaf(sv[p / SB][rr][p % SB], pp[rr], facc[j][rr]);
       }
       load_w(p, kb + PF);
       __builtin_amdgcn_sched_barrier(0);
