@@ -756,7 +756,9 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
   // their SB blocks for the lane's four columns, 4 SB bytes per column,
   // loaded with the last of those slots (when all of their previous blocks
   // are done); scales past the slice's last block belong to the next row or
-  // read zero, and multiply weights that read zero.
+  // read zero, and multiply zero products (the activations staged for those
+  // blocks read zero; their weight bytes read zero too, which INT4 decodes
+  // as code -8, not 0).
   constexpr int SB = PF < 4 ? PF : 4;
   static_assert(PF % SB == 0 && (SB == 4 || SB == 2), "scales load two or four K blocks at a time");
   typename WF::T wv[PF][2];
