@@ -22,7 +22,9 @@
 // dequantisation of chain t - 1 (one MFMA, then eight VALU ops, pinned with
 // sched_group_barrier), and the W fragments of the next chain pair are read
 // from LDS two chains ahead; the last chain of a K block is dequantised while
-// the next block's first MFMAs run.  The MFMA results must land in VGPRs for
+// the next block's first MFMAs run.  Without K parity the block's barrier
+// sits before its last chain row, so the next block's first fragments are
+// read, and the block after it loaded, while that row's MFMAs run.  The MFMA results must land in VGPRs for
 // the VALU: this file is compiled with the backend's VGPR-form MFMA option
 // (AGPR results would cost one v_accvgpr_read per output).  At NWM = 4 two
 // waves share each SIMD and the 256 x 256 tile moves 1 KB of operands per
@@ -375,15 +377,158 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
       drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, JM - 1>{}, sp,
             NK - 1 - ((NK - 1 - par) % KS));
   };
+  // The K loop without K parity, rotated across K blocks: the barrier of
+  // block kb sits before its last chain row (chain TB = JM (CI - 1)), where
+  // every wave has issued all its fragment reads of the block, so that the
+  // next block's first fragments are read from LDS, and block kb + 2 is
+  // loaded into the stage block kb leaves, while the last chains of block kb
+  // run; right after a barrier each wave has its next MFMA operands in
+  // registers instead of all eight waves reading them from LDS at once.
+  // Fragment registers: af[j] (A of fragment j), wc (W of the current chain
+  // row), wnx (W of the next chain row, then the next block's first row).
+  auto kloop_rot = [&](auto jmc) {
+    constexpr int JM = decltype(jmc)::value;
+    constexpr int TB = JM * (CI - 1);   // the chain the barrier precedes
+    auto stg = [&](int kb) { return smem + (kb & 1) * STG; };
+    auto rd_a = [&](v4i(&f)[4], const char* buf, int j) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) f[ks] = *(const v4i*)(buf + (wm * 64 + j * 32) * 128 + lo[ks]);
+    };
+    auto rd_w = [&](v4i(&f)[4], const char* buf, int i) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) f[ks] = *(const v4i*)(buf + BM * 128 + (wn * WC + i * 32) * 128 + lo[ks]);
+    };
+    // every wave, active or not, meets one barrier per block (the last
+    // block's included) and issues its loads of block kb + 2 (and of the
+    // next scale chunk)
+    // (branch-free: past the last block the loads' offsets lie outside the
+    // descriptors' ranges, so they move no data and write zeros into the
+    // stage block kb has left, which nothing reads again; rows past the
+    // tile read zeros through the descriptor)
+    auto sync_point = [&](int kb) {
+      waitcnt<0, 0>();   // block kb + 1 landed; own reads of block kb done
+      barrier();         // everyone's landed; everyone is past its reads of block kb
+      const int T = kb + 2;
+      const uint32_t so = T < NK ? 0u : 0x20000000u;
+      const uint32_t base = lds0 + (T & 1) * STG;
+#pragma unroll
+      for (int b = 0; b < AI; ++b) dma16(ra, voffA, b * K8 + T * 128 + so, base + (wave * AI + b) * 1024);
+#pragma unroll
+      for (int b = 0; b < WI; ++b) dma16(rw, voffW, b * K8 + T * 128 + so, base + BM * 128 + (wave * WI + b) * 1024);
+    };
+    if (NK > 0) BK_DMA(0)
+    waitcnt<0, 0>();
+    barrier();
+    if (NK > 1) BK_DMA(1)
+    v4i af[JM][4], wc[4], wnx[4];
+    if (wact && NK > 0) {
+      rd_a(af[0], stg(0), 0);
+      rd_w(wc, stg(0), 0);
+    }
+    for (int kb = 0; kb < NK; ++kb) {
+      // scale chunk c + 1 (slice blocks 16 (c + 1) ..) goes into the buffer
+      // chunk c - 1 used, once every wave is past the barrier of block 16 c
+      // (its last reads of chunk c - 1 were at block 16 c - 2); it is first
+      // read at block 16 c + 15
+      if constexpr (SCL)
+        if (kb >= 1 && ((kb - 1) & 15) == 0 && kb + 15 < NK) BK_SCL(((kb - 1) >> 4) + 1)
+      float sc0[NSW], sc1[NSW];
+#pragma unroll
+      for (int q = 0; q < NSW; ++q) {
+        sc0[q] = __fmul_rn(la0, lw[q]);
+        sc1[q] = __fmul_rn(la1, lw[q]);
+      }
+      if (DQ) {
+        const int kn = kb + 1 < NK ? kb + 1 : kb;
+        if constexpr (SCL) {
+          la0 = la_lds(sao[0], kn);
+          la1 = la_lds(sao[1], kn);
+        }
+#pragma unroll
+        for (int q = 0; q < NSW; ++q) lw[q] = sw_row[q][kn];
+      }
+      if (!wact) {
+        sync_point(kb);
+        continue;
+      }
+      const char* buf = stg(kb);
+#pragma unroll
+      for (int t = 0; t < JM * CI; ++t) {
+        const int i = t / JM, j = t % JM;
+        if (t == TB) {
+          sync_point(kb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // LDS reads riding along this chain's MFMAs: the second fragment's A
+        // (chain 0), the next chain row's W, and from the barrier on the next
+        // block's first W row and first A fragment (in the last block these
+        // read the other stage's stale bytes, never used)
+        int nrd = 0;
+        if (JM == 2 && t == 0) {
+          rd_a(af[1], buf, 1);
+          nrd += 4;
+        }
+        if (j == 0 && i < CI - 1) {
+          rd_w(wnx, buf, i + 1);
+          nrd += 4;
+        } else if (t == TB) {
+          rd_w(wnx, stg(kb + 1), 0);
+          nrd += 4;
+        }
+        if (JM == 2 && t == TB + 1) {
+          rd_a(af[0], stg(kb + 1), 0);
+          nrd += 4;
+        }
+        v16i c = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_i32_32x32x32_i8(wc[ks], af[j][ks], c, 0, 0, 0);
+        if (t == 0) {
+          if (kb > 0) drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, JM - 1>{}, sp, kb - 1);
+        } else {
+          const int tp = t - 1;
+#define BK_DRAIN(IP, JP)                                                                                     \
+  if (JP < JM && tp == IP * JM + JP)                                                                         \
+    drain(pp, std::integral_constant<int, IP>{}, std::integral_constant<int, JP>{}, (JP == 0 ? sc0 : sc1)[QI(IP)], kb);
+          BK_DRAIN(0, 0) BK_DRAIN(0, 1) BK_DRAIN(1, 0) BK_DRAIN(1, 1)
+          BK_DRAIN(2, 0) BK_DRAIN(2, 1) BK_DRAIN(3, 0)
+#undef BK_DRAIN
+        }
+        // one MFMA, then eight VALU ops, four times; the reads ride along
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          if (nrd == 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (nrd == 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pp = c;
+        if (j == JM - 1 && i < CI - 1) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) wc[ks] = wnx[ks];
+        }
+      }
+      sp = (JM == 2 ? sc1 : sc0)[QI(CI - 1)];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) wc[ks] = wnx[ks];
+      if (JM == 1) rd_a(af[0], stg(kb + 1), 0);
+    }
+    if (NK > 0 && wact)
+      drain(pp, std::integral_constant<int, CI - 1>{}, std::integral_constant<int, JM - 1>{}, sp, NK - 1);
+  };
   // Waves whose second fragment has no rows run a K loop of their own
   // (a branch inside the loop would tie both forms to one register
   // assignment); only the grouped 256-row tiles, where MoE experts of
   // 129-160 rows leave such a wave beside a full one on a SIMD, have it.
-  if constexpr (MODE == MODE_GROUPED && NWM == 4) {
-    if (wm * 64 + 32 >= mrows)   // (with wact) only the first fragment has rows
-      kloop(std::integral_constant<int, 1>{});
-    else
-      kloop(std::integral_constant<int, 2>{});
+  if constexpr (KS == 1) {
+    if constexpr (MODE == MODE_GROUPED && NWM == 4) {
+      if (wm * 64 + 32 >= mrows)   // (with wact) only the first fragment has rows
+        kloop_rot(std::integral_constant<int, 1>{});
+      else
+        kloop_rot(std::integral_constant<int, 2>{});
+    } else {
+      kloop_rot(std::integral_constant<int, 2>{});
+    }
   } else {
     kloop(std::integral_constant<int, 2>{});
   }
