@@ -464,9 +464,11 @@ __global__ __launch_bounds__(64 * NWM * NWN * (KP ? 2 : 1), 1) void k_gemm_block
         // block's first W row and first A fragment (in the last block these
         // read the other stage's stale bytes, never used)
         int nrd = 0;
-        if (JM == 2 && t == 0) {
-          rd_a(af[1], buf, 1);
-          nrd += 4;
+        if constexpr (JM == 2) {
+          if (t == 0) {
+            rd_a(af[1], buf, 1);
+            nrd += 4;
+          }
         }
         if (j == 0 && i < CI - 1) {
           rd_w(wnx, buf, i + 1);
