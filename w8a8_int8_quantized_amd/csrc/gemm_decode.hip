@@ -684,22 +684,29 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a16(const uint16_t* __rest
 // with the fragment layout of k_decode_w8a16.  A staged row holds 128 fp16
 // values (256 bytes, 16 chunks of 16 bytes); chunk c of row r is stored at
 // c ^ (r & 15).
-template <int MF, int NWV, int G, int PF, bool W4 = false>
-__global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __restrict__ x,
+// KPAR = 2: twice the waves, the second NWV taking the odd K blocks (each
+// wave's ring then holds every other block, and a staged group of G = 2
+// blocks is one step for both halves); the odd sums are added to the even
+// ones through LDS at the end (even + odd).
+template <int MF, int NWV, int G, int PF, bool W4 = false, int KPAR = 1>
+__global__ __launch_bounds__(64 * NWV * KPAR) void k_w8a16_shared(const uint16_t* __restrict__ x,
                                                            const uint8_t* __restrict__ W,
                                                            const float* __restrict__ ws, uint16_t* __restrict__ Y,
                                                            int M, int N, int K) {
+  static_assert(KPAR == 1 || (KPAR == 2 && G == 2), "K parity: a staged group is the two halves' blocks");
   using WF = WFrag<W4>;
   const int KW = W4 ? K >> 1 : K;   // bytes per weight row
   constexpr int ROWS = 16 * MF;
   constexpr int CHUNKS = ROWS * 16;
-  constexpr int NT = 64 * NWV;
+  constexpr int NT = 64 * NWV * KPAR;
   constexpr int AG = (G * CHUNKS + NT - 1) / NT;
   __shared__ v4i xs[2][G * CHUNKS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wcol = KPAR == 1 ? wave : wave % NWV;   // the wave's 16 columns
+  const int par = KPAR == 1 ? 0 : wave / NWV;       // its first K block
   const int q = lane >> 4;
-  const int nw = blockIdx.x * 16 * NWV + 16 * wave;
+  const int nw = blockIdx.x * 16 * NWV + 16 * wcol;
   const int KBt = K >> 7;
   // split-K: slice blockIdx.y of gridDim.y covers K blocks kbs .. kbe - 1;
   // every descriptor starts at the slice's first block (rows past the end
@@ -751,28 +758,35 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
     for (int i = 0; i < AG; ++i)
       if (xpos[i] >= 0) xs[buf][xpos[i]] = xreg[i];
   };
-  // The ring holds consecutive K blocks, slot p block it PF + p.  Slots
-  // SB i .. SB i + SB - 1 (SB = 4, or PF if less) share the scales sv[i] of
-  // their SB blocks for the lane's four columns, 4 SB bytes per column,
-  // loaded with the last of those slots (when all of their previous blocks
-  // are done); scales past the slice's last block belong to the next row or
+  // The ring holds the wave's consecutive steps, slot p step it PF + p, step
+  // t being K block KPAR t + par.  Slots SB i .. SB i + SB - 1 (SB = 4, or
+  // PF if less; 2 with K parity) share the scales sv[i] of their SB blocks
+  // for the lane's four columns, loaded with the last of those slots (when
+  // all of their previous blocks are done): 4 SB consecutive bytes per
+  // column, or with K parity 16 bytes covering the pair's blocks kf and
+  // kf + 2; scales past the slice's last block belong to the next row or
   // read zero, and multiply zero products (the activations staged for those
   // blocks read zero; their weight bytes read zero too, which INT4 decodes
   // as code -8, not 0).
-  constexpr int SB = PF < 4 ? PF : 4;
+  constexpr int SB = KPAR == 2 ? 2 : (PF < 4 ? PF : 4);
   static_assert(PF % SB == 0 && (SB == 4 || SB == 2), "scales load two or four K blocks at a time");
   typename WF::T wv[PF][2];
   float sv[PF / SB][4][SB];
-  auto load_w = [&](int P, int kb) {
+  auto load_w = [&](int P, int t) {
+    const int kb = KPAR * t + par;
     const uint32_t ko = kb < KB ? (uint32_t)kb * WF::kBytesPerGroup : kOob;
     wv[P][0] = WF::load(rw, woff + ko);
     wv[P][1] = WF::load(rw, woff + ko + WF::kBytesPerGroup / 2);
     if (P % SB == SB - 1) {
-      const int kf = kb - (SB - 1);   // the first block of the group
+      const int kf = kb - KPAR * (SB - 1);   // the block of the group's first slot
       const uint32_t so = kf < KB ? (uint32_t)kf * 4u : kOob;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (SB == 4) {
+        if constexpr (KPAR == 2) {
+          const v4f t4 = __builtin_bit_cast(v4f, bl16(rs, soff + r * KBt * 4 + so));
+          sv[P / SB][r][0] = t4[0];
+          sv[P / SB][r][1] = t4[2];
+        } else if constexpr (SB == 4) {
           const v4f t = __builtin_bit_cast(v4f, bl16(rs, soff + r * KBt * 4 + so));
 #pragma unroll
           for (int e = 0; e < 4; ++e) sv[P / SB][r][e] = t[e];
@@ -798,14 +812,15 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
   waitcnt<63, 0>();
   barrier();
 
-  const int iters = (NG * G + PF - 1) / PF;
+  // steps: K blocks (K parity: pairs of blocks, one staged group each)
+  const int iters = (KPAR == 1 ? NG * G + PF - 1 : NG + PF - 1) / PF;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int kb = it * PF + p;
-      const int g = it * (PF / G) + p / G;
+      const int t = it * PF + p;
+      const int g = KPAR == 1 ? it * (PF / G) + p / G : t;
       const int buf = g & 1;
-      const int bo = (p % G) * CHUNKS;
+      const int bo = KPAR == 1 ? (p % G) * CHUNKS : par * CHUNKS;
       v8h wh[4];
       WF::to_f16(wv[p][0], wv[p][1], wh);
 #pragma unroll
@@ -821,15 +836,32 @@ __global__ __launch_bounds__(64 * NWV) void k_w8a16_shared(const uint16_t* __res
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) facc[j][rr] = __builtin_fmaf(sv[p / SB][rr][p % SB], pp[rr], facc[j][rr]);
       }
-      load_w(p, kb + PF);
+      load_w(p, t + PF);
       __builtin_amdgcn_sched_barrier(0);
-      if (p % G == G - 1) {
+      if (KPAR == 2 || p % G == G - 1) {
         store_act(buf ^ 1);
         load_act(g + 2);
         __builtin_amdgcn_sched_barrier(0);
         waitcnt<63, 0>();
         barrier();
       }
+    }
+  }
+  if constexpr (KPAR == 2) {
+    // every wave is past its reads of xs (the loop ends with a barrier):
+    // the odd-block sums through it, added to the even ones (even + odd)
+    v4f* red = reinterpret_cast<v4f*>(&xs[0][0]) + wcol * MF * 64 + lane;
+    if (par == 1) {
+#pragma unroll
+      for (int j = 0; j < MF; ++j) red[j * 64] = facc[j];
+    }
+    barrier();
+    if (par == 1) return;
+#pragma unroll
+    for (int j = 0; j < MF; ++j) {
+      const v4f o = red[j * 64];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) facc[j][r] = __fadd_rn(facc[j][r], o[r]);
     }
   }
 
@@ -1018,35 +1050,39 @@ hipError_t w8a16_launch(const uint16_t* x, const uint8_t* W, const float* s, uin
   return hipGetLastError();
 }
 
-template <int MF, int NWV, int PF, bool W4>
+template <int MF, int NWV, int PF, bool W4, int KPAR>
 hipError_t w8a16_shared_launch(const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y, int M, int64_t N,
                                int64_t K, int S, hipStream_t st) {
   const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)), (unsigned)S);
-  hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2, PF, W4>), g, dim3(64 * NWV), 0, st, x, W, s, Y, M, (int)N, (int)K);
+  hipLaunchKernelGGL((k_w8a16_shared<MF, NWV, 2, PF, W4, KPAR>), g, dim3(64 * NWV * KPAR), 0, st, x, W, s, Y, M,
+                     (int)N, (int)K);
   return hipGetLastError();
 }
 
-template <int MF, int NWV, bool W4>
+template <int MF, int NWV, bool W4, int KPAR>
 hipError_t w8a16_shared_depth(int pf, int S, const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y, int M,
                               int64_t N, int64_t K, hipStream_t st) {
   if constexpr (NWV <= 4) {
-    if (pf == 8) return w8a16_shared_launch<MF, NWV, 8, W4>(x, W, s, Y, M, N, K, S, st);
+    if (pf == 8) return w8a16_shared_launch<MF, NWV, 8, W4, KPAR>(x, W, s, Y, M, N, K, S, st);
   }
   if constexpr (NWV <= 8) {
-    if (pf >= 4) return w8a16_shared_launch<MF, NWV, 4, W4>(x, W, s, Y, M, N, K, S, st);
+    if (pf >= 4) return w8a16_shared_launch<MF, NWV, 4, W4, KPAR>(x, W, s, Y, M, N, K, S, st);
   }
-  return w8a16_shared_launch<MF, NWV, 2, W4>(x, W, s, Y, M, N, K, S, st);
+  return w8a16_shared_launch<MF, NWV, 2, W4, KPAR>(x, W, s, Y, M, N, K, S, st);
 }
 
-template <int MF, bool W4>
+template <int MF, bool W4, int KPAR = 1>
 hipError_t w8a16_shared_width(int nwv, int pf, int S, const uint16_t* x, const uint8_t* W, const float* s, uint16_t* Y,
                               int M, int64_t N, int64_t K, hipStream_t st) {
   switch (nwv) {
-    case 3: return w8a16_shared_depth<MF, 3, W4>(pf, S, x, W, s, Y, M, N, K, st);
-    case 4: return w8a16_shared_depth<MF, 4, W4>(pf, S, x, W, s, Y, M, N, K, st);
-    case 6: return w8a16_shared_depth<MF, 6, W4>(pf, S, x, W, s, Y, M, N, K, st);
-    case 8: return w8a16_shared_depth<MF, 8, W4>(pf, S, x, W, s, Y, M, N, K, st);
-    default: return w8a16_shared_depth<MF, 9, W4>(pf, S, x, W, s, Y, M, N, K, st);
+    case 3: return w8a16_shared_depth<MF, 3, W4, KPAR>(pf, S, x, W, s, Y, M, N, K, st);
+    case 4: return w8a16_shared_depth<MF, 4, W4, KPAR>(pf, S, x, W, s, Y, M, N, K, st);
+    case 6: return w8a16_shared_depth<MF, 6, W4, KPAR>(pf, S, x, W, s, Y, M, N, K, st);
+    case 8: return w8a16_shared_depth<MF, 8, W4, KPAR>(pf, S, x, W, s, Y, M, N, K, st);
+    default:
+      // nine waves twice over would exceed a workgroup's 16 waves
+      if constexpr (KPAR == 1) return w8a16_shared_depth<MF, 9, W4, 1>(pf, S, x, W, s, Y, M, N, K, st);
+      else return hipErrorInvalidConfiguration;
   }
 }
 
@@ -1092,12 +1128,17 @@ hipError_t group16_dispatch(const uint16_t* x, const uint8_t* W, const float* s,
   const int min_shared = nwv0 > 0 ? 5 : 17;   // fewest rows a slice takes to the shared kernel
   const int64_t wgs1 = (N + 16 * nwv - 1) / (16 * nwv);
   const int64_t KBt = K >> 7;
+  // from 17 rows the workgroup runs twice its waves, the second half on the
+  // odd K blocks (K parity): more waves per CU to hide the activation
+  // staging and load latency without another split of K (a workgroup holds
+  // at most 16 waves)
+  const int kpar = M >= 17 && nwv <= 8 ? 2 : 1;
   int S = 1;
   // (from 32 rows one workgroup per CU: the slices' partials and their
   // reduction then cost more than the second workgroup's latency hiding)
   const int64_t target = M >= 32 ? kCUs : 2 * kCUs;
   while (wgs1 * S < target && S < 8 && KBt / (2 * S) >= 4) S *= 2;
-  const int64_t wpc = nwv * ((wgs1 * S + kCUs - 1) / kCUs);
+  const int64_t wpc = nwv * kpar * ((wgs1 * S + kCUs - 1) / kCUs);
   const int pf = wpc <= 4 ? 8 : (wpc <= 8 ? 4 : 2);
   // slices' fp32 partials in the stream's scratch, held until every
   // reduction below is enqueued
@@ -1112,9 +1153,14 @@ hipError_t group16_dispatch(const uint16_t* x, const uint8_t* W, const float* s,
     hipError_t e;
     if (mm >= min_shared) {
       uint16_t* dst = S > 1 ? reinterpret_cast<uint16_t*>(part) : ys;
-      e = mm <= 16 ? w8a16_shared_width<1, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
-          : mm <= 32 ? w8a16_shared_width<2, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
-                   : w8a16_shared_width<4, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st);
+      if (kpar == 2)
+        e = mm <= 16 ? w8a16_shared_width<1, W4, 2>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+            : mm <= 32 ? w8a16_shared_width<2, W4, 2>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+                     : w8a16_shared_width<4, W4, 2>(nwv, pf, S, xs, W, s, dst, mm, N, K, st);
+      else
+        e = mm <= 16 ? w8a16_shared_width<1, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+            : mm <= 32 ? w8a16_shared_width<2, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st)
+                     : w8a16_shared_width<4, W4>(nwv, pf, S, xs, W, s, dst, mm, N, K, st);
       if (e == hipSuccess && S > 1) {
         const dim3 rg((unsigned)((mm * ((N + 3) / 4) + 255) / 256));
         hipLaunchKernelGGL(k_w16_slices_sum, rg, dim3(256), 0, st, part, S, mm, (int)N, ys);
