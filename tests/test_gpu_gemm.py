@@ -18,7 +18,7 @@ import torch
 
 import synth
 import w8a8_int8_quantized_amd as w8
-from oracle import formats, gemm, quant, routing
+from oracle import formats, gemm, int4, quant, routing
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -292,6 +292,26 @@ def test_w8a16_split_k_odd_n():
     yn = _np(w8.gemm_w8a16_group(X, W, SW)).astype(np.float32)
     e32, e64 = gemm.normwise_rel_err(yn, y32), gemm.normwise_rel_err(yn, y64)
     assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+
+
+# From 17 rows the shared-activation kernel runs twice its waves, the second
+# half on the odd K blocks: an odd number of K blocks per slice (K = 1152 in
+# two slices of 4 and 5 blocks at 20 and 24 rows on the balanced 12288
+# columns; unsplit K = 1920 at 40 rows), INT8 and INT4 weights.
+@pytest.mark.parametrize("M,K", [(20, 1152), (24, 1152), (40, 1920)])
+def test_w8a16_k_parity_odd_blocks(M, K):
+    N = 12288
+    x, qw, sw = _w8a16_case(M, N, K, seed=M + K)
+    y64, y32 = gemm.gemm_w8a16_group(x, qw, sw)
+    X, W, SW = _dev(x, qw, sw)
+    yn = _np(w8.gemm_w8a16_group(X, W, SW)).astype(np.float32)
+    e32, e64 = gemm.normwise_rel_err(yn, y32), gemm.normwise_rel_err(yn, y64)
+    assert e32 <= TOL32 and e64 <= TOL64, (e32, e64)
+    w = synth.weights(N, K, seed=M + K + 1, dtype=torch.float16)
+    q4, s4 = w8.quant_weight_int4_group(w.to(DEV))
+    y4 = _np(w8.gemm_w4a16_group(X, q4, s4)).astype(np.float32)
+    y4r = _np(w8.gemm_w8a16_group(X, torch.from_numpy(int4.unpack_int4(_np(q4))).to(DEV), s4)).astype(np.float32)
+    assert np.array_equal(y4, y4r)
 
 
 def test_w8a16_split_k_repeated_calls():
