@@ -153,6 +153,23 @@ def test_block_gemm_tile_widths(M, N, K):
     assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
 
 
+# 256-row tiles (a grid of at least 256 of them, unsplit) with one, two and
+# three K blocks: the block loop's barrier before the last chain row, the
+# stage loads past the last block, and the next block's fragments read from
+# the other stage in the last block; M and N ragged.
+@pytest.mark.parametrize("K", [128, 256, 384])
+def test_block_gemm_256_row_tiles_short_k(K):
+    M, N = 2000, 8000
+    qa, sa, qw, sw = _inputs(M, N, K, seed=K + 11, scheme="block")
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    _, y64, y32 = gemm.gemm_block(qa, sa, qw, sw)
+    yf = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32)
+    e32, e64 = gemm.normwise_rel_err(_np(yf), y32), gemm.normwise_rel_err(_np(yf), y64)
+    assert e32 <= 1e-5 and e64 <= TOL64, (e32, e64)
+    yb = w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.bfloat16)
+    assert np.array_equal(_np(yb.view(torch.int16)).view(np.uint16), _bf16_of(yf))
+
+
 def test_block_equals_channel_when_k_is_one_block():
     M, N, K = 70, 256, 128
     qa, sa, qw, sw = _inputs(M, N, K, seed=1, scheme="block")
