@@ -251,6 +251,36 @@ def test_block_rows_independent_of_next_row_scale(M, N):
     assert e32 <= 1e-5 and gemm.normwise_rel_err(yf[good], y64) <= TOL64, e32
 
 
+# The workgroup-shared block-wise decode kernel stages a tile's activation
+# scales in LDS (16 MF rows of K/128 | 1 floats, at most 64 KB): at 64 rows
+# K = 32640 (255 K blocks, an odd row stride with no padding) is the longest
+# staged, and K = 32768 (256 blocks) runs the split-K decode kernel instead.
+# K = 7296 (57 blocks) and 7424 (58, a padded row) exercise the blocks past
+# the last of an odd and an even count.  Checked on three sampled 128-column
+# weight blocks; an infinite scale at the start of row 4 must reach no other
+# row (past the end of row 3's staged scales lies row 4's).
+@pytest.mark.parametrize("M,K", [(64, 32640), (64, 32768), (40, 7296), (40, 7424)])
+def test_block_decode_staged_scales(M, K):
+    N = 12288
+    rng = np.random.default_rng(K)
+    NB = N // 128
+    blocks = np.array(sorted({0, NB - 1, int(rng.integers(1, NB - 1))}))
+    cols = np.concatenate([np.arange(b * 128, (b + 1) * 128) for b in blocks])
+    qw, sw = quant.quant_weight_block(synth.to_numpy(synth.weights(N, K, seed=K + 1)))
+    qa, sa = quant.quant_act_group(synth.to_numpy(synth.activations(M, K, seed=K + 2)))
+    sa = sa.copy()
+    sa[4, 0] = np.float32(np.inf)
+    A, SA, W, SW = _dev(qa, sa, qw, sw)
+    qwc, swb = qw[cols], sw[blocks]
+    del qw
+    yf = _np(w8.gemm_w8a8_block(A, SA, W, SW, out_dtype=torch.float32))[:, cols]
+    good = [m for m in range(M) if m != 4]
+    _, y64, y32 = gemm.gemm_block(qa[good], sa[good], qwc, swb)
+    assert np.isfinite(yf[good]).all()
+    e32 = gemm.normwise_rel_err(yf[good], y32)
+    assert e32 <= 1e-5 and gemm.normwise_rel_err(yf[good], y64) <= TOL64, e32
+
+
 # N = 1000 is not a multiple of the 64-column workgroup: the last workgroup's
 # fourth wave owns no columns, and K is split over 8 workgroups (slices past
 # the first start their descriptors mid-row).  Regression case for such a wave

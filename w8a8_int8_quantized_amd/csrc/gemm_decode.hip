@@ -253,7 +253,12 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restric
 // through a PF-deep ring (PF a multiple of G).  No cross-wave reduction: every
 // wave covers all of K for its columns.  The dispatcher sizes workgroups so
 // that the grid splits evenly over the CUs (the weight stream runs at the pace
-// of the most loaded CU).
+// of the most loaded CU).  Block-wise (MODE 0), the activation scales of all
+// K blocks ([16 MF][KB] floats, rows past M zero) are staged in dynamic LDS
+// once, before the loop, by consecutive dword loads of the row-major array
+// (a row's scales in one place, rather than one cache line per row and
+// group); rows are stored KB | 1 floats apart, an odd stride, so the 16 rows
+// a fragment read touches fall in distinct banks.
 template <int MODE, int MF, int NWV, int G, int PF, int OUT>
 __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                         const int8_t* __restrict__ W, const float* __restrict__ sw,
@@ -263,9 +268,8 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
   constexpr int CHUNKS = ROWS * 8;                               // 16-byte chunks per block
   constexpr int NT = 64 * NWV;                                   // threads
   constexpr int AG = (G * CHUNKS + NT - 1) / NT;                 // chunks per thread per group
-  constexpr int SG = (G * ROWS + NT - 1) / NT;                   // block scales per thread per group
   __shared__ v4i as[2][G * CHUNKS];
-  __shared__ float ss[2][G * ROWS];
+  extern __shared__ float ssa[];   // MODE 0: ROWS rows of KB | 1 floats
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
@@ -299,19 +303,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
     aoff[i] = ok ? (uint32_t)(r * K + bk * 128 + col * 16) : kOob;
     apos[i] = ok ? bk * CHUNKS + r * 8 + (col ^ (r & 7)) : -1;
   }
-  // block scale i of a group: K block sbk[i] of the group; blocks past the
-  // last read zero (past the end of a row lies the next row's first scale,
-  // and an infinite one there must not reach this row through a zero partial)
-  uint32_t soff[SG];
-  int spos[SG], sbk[SG];
-#pragma unroll
-  for (int i = 0; i < SG; ++i) {
-    const int e = threadIdx.x + i * NT;
-    const bool ok = MODE == 0 && e < G * ROWS;
-    soff[i] = ok ? (uint32_t)((e % ROWS) * KB * 4 + (e / ROWS) * 4) : kOob;
-    spos[i] = ok ? e : -1;
-    sbk[i] = e / ROWS;
-  }
+  const int SST = KB | 1;   // row stride of the staged activation scales
 
   v4f facc[FNW][MF];
   v4i iacc[FNW][MF];
@@ -324,25 +316,36 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
     }
 
   v4i areg[AG];
-  float sreg[SG];
-  auto load_act = [&](int g) {  // group g's activations and block scales into registers
+  auto load_act = [&](int g) {  // group g's activations into registers
     const uint32_t ko = g < NG ? (uint32_t)g * G * 128u : kOob;
 #pragma unroll
     for (int i = 0; i < AG; ++i) areg[i] = bl16(ra, aoff[i] + ko);
-    if (MODE == 0) {
-      const int left = KB - g * G;
-#pragma unroll
-      for (int i = 0; i < SG; ++i) sreg[i] = blf(rsa, soff[i] + (sbk[i] < left ? (uint32_t)g * G * 4u : kOob));
-    }
   };
   auto store_act = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < AG; ++i)
       if (apos[i] >= 0) as[buf][apos[i]] = areg[i];
-    if (MODE == 0) {
+  };
+  // the activation scales of every K block (MODE 0): flat element e of
+  // [ROWS][KB], past M * KB zero; sixteen dword loads per thread at a time
+  constexpr int SCH = 16;
+  const int stot = ROWS * KB;
+  float sv[SCH];
+  auto scl_load = [&](int e0) {
 #pragma unroll
-      for (int i = 0; i < SG; ++i)
-        if (spos[i] >= 0) ss[buf][spos[i]] = sreg[i];
+    for (int i = 0; i < SCH; ++i) {
+      const int e = e0 + i * NT + (int)threadIdx.x;
+      sv[i] = blf(rsa, e < stot ? (uint32_t)e * 4u : kOob);
+    }
+  };
+  auto scl_store = [&](int e0) {
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int e = e0 + i * NT + (int)threadIdx.x;
+      if (e < stot) {
+        const int r = e / KB;
+        ssa[r * SST + (e - r * KB)] = sv[i];
+      }
     }
   };
   v4i wv[PF][FNW][2];
@@ -358,7 +361,9 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
   };
 
   // prologue, issued in the order the loop issues: group 0 staged, then the
-  // weight ring, then group 1
+  // weight ring, then group 1 (the scales' first loads go out first and are
+  // stored once the ring is on its way)
+  if constexpr (MODE == 0) scl_load(0);
   load_act(0);
   store_act(0);
   __builtin_amdgcn_sched_barrier(0);
@@ -369,6 +374,13 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
   }
   load_act(1);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MODE == 0) {
+    scl_store(0);
+    for (int e0 = SCH * NT; e0 < stot; e0 += SCH * NT) {
+      scl_load(e0);
+      scl_store(e0);
+    }
+  }
   waitcnt<63, 0>();
   barrier();
 
@@ -395,7 +407,10 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_shared(const int8_t* __rest
           const int r = 16 * (j0 + jj) + (lane & 15);
           af[jj][0] = as[buf][bo + r * 8 + (q ^ (r & 7))];
           af[jj][1] = as[buf][bo + r * 8 + ((4 + q) ^ (r & 7))];
-          if (MODE == 0) saj[jj] = ss[buf][(p % G) * ROWS + r];
+          // blocks past the last take a zero scale (past a row's end lie
+          // the padding and the next row, whose scale may be infinite and
+          // must not meet this row's zero partial)
+          if (MODE == 0) saj[jj] = kb < KB ? ssa[r * SST + kb] : 0.f;
         }
 #pragma unroll
         for (int f = 0; f < FNW; ++f)
@@ -960,11 +975,17 @@ inline int pick_ring_depth(int64_t N, int nwv) {
   return waves_per_cu <= 4 ? 8 : (waves_per_cu <= 8 ? 4 : 2);
 }
 
+// Dynamic LDS of the block-wise shared-activation kernel: 16 MF rows of
+// activation scales, KB | 1 floats apart.
+inline size_t shared_scale_lds(int MF, int64_t K) { return (size_t)16 * MF * ((K >> 7) | 1) * 4; }
+constexpr size_t kSharedScaleLdsMax = 64 * 1024;
+
 template <int MODE, int MF, int NWV, int PF, int OUT>
 hipError_t shared_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
                          int64_t N, int64_t K, hipStream_t st) {
   const dim3 g((unsigned)((N + 16 * NWV - 1) / (16 * NWV)));
-  hipLaunchKernelGGL((k_decode_shared<MODE, MF, NWV, 2, PF, OUT>), g, dim3(64 * NWV), 0, st, A, sa, W, sw, Y,
+  const size_t lds = MODE == 0 ? shared_scale_lds(MF, K) : 0;
+  hipLaunchKernelGGL((k_decode_shared<MODE, MF, NWV, 2, PF, OUT>), g, dim3(64 * NWV), lds, st, A, sa, W, sw, Y,
                      (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
@@ -1019,7 +1040,10 @@ inline int pick_shared_width(int64_t N) {
 template <int MODE, int OUT>
 hipError_t decode_dispatch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
                            int64_t N, int64_t K, hipStream_t st) {
-  const int nwv = pick_shared_width(N);
+  int nwv = pick_shared_width(N);
+  // block-wise: the staged activation scales must fit their LDS budget
+  // (K up to 32640 at 64 rows); longer K runs the split-K decode kernel
+  if (MODE == 0 && shared_scale_lds(M <= 16 ? 1 : (M <= 32 ? 2 : 4), K) > kSharedScaleLdsMax) nwv = 0;
   if (nwv > 0) {
     if (M <= 16) return shared_width<MODE, 1, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
     if (M <= 32) return shared_width<MODE, 2, OUT>(nwv, A, sa, W, sw, Y, M, N, K, st);
