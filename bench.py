@@ -353,6 +353,21 @@ def rows(args):
             out[f"decode_fused_block_quant_m{M}"] = e
         del wsets
         torch.cuda.empty_cache()
+        # --- the down projection of the same MLP at decode (K = 18432, N = 7168: the
+        # split-K decode kernel, N giving no balanced shared grid), 8 weight copies (1.06 GB)
+        K, N = DOWN
+        wsets = []
+        for s in range(8):
+            w = synth.weights(N, K, seed=synth.SEEDS["decode"] + 10 + s, device=dev)
+            wsets.append(w8.quant_weight_block(w))
+            del w
+        for M in (1, 8, 32, 64):
+            qa, sa = w8.quant_act_group(synth.activations(M, K, seed=M + 100, device=dev))
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            ms = time_calls(lambda i: w8.gemm_w8a8_block(qa, sa, wsets[i][0], wsets[i][1], out=y), 8, R)
+            out[f"decode_block_down_m{M}"] = gemm_entry(ms, M, N, K, N * K + 4 * ((N + 127) // 128) * (K // 128))
+        del wsets
+        torch.cuda.empty_cache()
 
     if want("asym"):
         # --- asymmetric per-tensor activations: quantiser (two passes over x;

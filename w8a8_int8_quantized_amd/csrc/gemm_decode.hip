@@ -99,11 +99,17 @@ __device__ __forceinline__ float blf(rsrc_t r, uint32_t off) {
 // weight row n0 + 16 f + (l & 15) and activation row 16 j + (l & 15), K bytes
 // 16 q .. 16 q + 15 (q = l >> 4) of each 64-wide half of the K block; the
 // result lane holds columns n0 + 16 f + 4 q + r (r = 0..3) of row 16 j + (l & 15).
-template <int MODE, int MF, int FNW, int SK, int PF, int OUT>
+// STS (MODE 0): the activation scales of all K blocks ([16 MF][KB] floats,
+// rows past M zero, rows KB | 1 floats apart) are staged in dynamic LDS
+// before the loop, as in k_decode_shared, instead of one scale load per
+// fragment row, block and lane (a cache line per row).
+template <int MODE, int MF, int FNW, int SK, int PF, int OUT, bool STS = false>
 __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restrict__ A, const float* __restrict__ sa,
                                                          const int8_t* __restrict__ W, const float* __restrict__ sw,
                                                          void* __restrict__ Y, int M, int N, int K) {
+  static_assert(!STS || MODE == 0, "staged scales: block-wise");
   __shared__ v4i red[SK][64];
+  extern __shared__ float dss[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
@@ -152,15 +158,45 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restric
     for (int j = 0; j < MF; ++j) {
       av[P][j][0] = bl16(ra, aoff[j] + ko);
       av[P][j][1] = bl16(ra, aoff[j] + ko + 64);
-      if (MODE == 0) ssa[P][j] = blf(rsa, saoff[j] + so);
+      if (MODE == 0 && !STS) ssa[P][j] = blf(rsa, saoff[j] + so);
     }
   };
+  constexpr int NT = 64 * SK, SCH = 16;
+  const int SST = KB | 1;
+  const int stot = 16 * MF * KB;
+  float sv[SCH];
+  auto scl_load = [&](int e0) {
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int e = e0 + i * NT + (int)threadIdx.x;
+      sv[i] = blf(rsa, e < stot ? (uint32_t)e * 4u : kOob);
+    }
+  };
+  auto scl_store = [&](int e0) {
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int e = e0 + i * NT + (int)threadIdx.x;
+      if (e < stot) {
+        const int r = e / KB;
+        dss[r * SST + (e - r * KB)] = sv[i];
+      }
+    }
+  };
+  if constexpr (STS) scl_load(0);
   // the prologue issues the slots in ring order (the scheduler would reverse
   // them, and the loop would then wait for the whole ring on every pass)
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     load(p, wave + p * SK);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (STS) {
+    scl_store(0);
+    for (int e0 = SCH * NT; e0 < stot; e0 += SCH * NT) {
+      scl_load(e0);
+      scl_store(e0);
+    }
+    __syncthreads();
   }
   // this wave's K blocks: wave, wave + SK, ...; PF of them per iteration, the
   // slots past the end hold zeros
@@ -179,7 +215,11 @@ __global__ __launch_bounds__(64 * SK) void k_decode_w8a8(const int8_t* __restric
           if (MODE == 0) {
             v4i pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][0], av[p][j][0], (v4i){0, 0, 0, 0}, 0, 0, 0);
             pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[p][f][1], av[p][j][1], pp, 0, 0, 0);
-            const float s = __fmul_rn(ssa[p][j], ssw[p][f]);
+            // slot p holds block kb0 + p SK; blocks past the last take a
+            // zero scale (past a row's end lie the padding and the next row)
+            const int kbp = kb0 + p * SK;
+            const float sap = STS ? (kbp < KB ? dss[(16 * j + (lane & 15)) * SST + kbp] : 0.f) : ssa[p][j];
+            const float s = __fmul_rn(sap, ssw[p][f]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) facc[f][j][r] = __builtin_fmaf(s, (float)pp[r], facc[f][j][r]);
           } else {
@@ -950,6 +990,11 @@ inline int pick_sk(int64_t workgroups, int64_t kblocks, int max_sk, int waves_pe
   return 1;
 }
 
+// Dynamic LDS of the block-wise decode kernels' staged scales: 16 MF rows of
+// activation scales, KB | 1 floats apart.
+inline size_t shared_scale_lds(int MF, int64_t K) { return (size_t)16 * MF * ((K >> 7) | 1) * 4; }
+constexpr size_t kSharedScaleLdsMax = 64 * 1024;
+
 template <int MODE, int MF, int FNW, int PF, int OUT>
 hipError_t decode_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
                          int64_t N, int64_t K, int waves_per_simd, hipStream_t st) {
@@ -957,6 +1002,17 @@ hipError_t decode_launch(const int8_t* A, const float* sa, const int8_t* W, cons
   const int sk = pick_sk(wgs, K >> 7, 8, waves_per_simd);
   const dim3 g((unsigned)wgs);
   const int m = (int)M, n = (int)N, k = (int)K;
+  // block-wise: activation scales staged in LDS where they fit the budget
+  const size_t lds = shared_scale_lds(MF, K);
+  if (MODE == 0 && lds <= kSharedScaleLdsMax) {
+    switch (sk) {
+      case 8: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 8, PF, OUT, MODE == 0>), g, dim3(512), lds, st, A, sa, W, sw, Y, m, n, k); break;
+      case 4: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 4, PF, OUT, MODE == 0>), g, dim3(256), lds, st, A, sa, W, sw, Y, m, n, k); break;
+      case 2: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 2, PF, OUT, MODE == 0>), g, dim3(128), lds, st, A, sa, W, sw, Y, m, n, k); break;
+      default: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 1, PF, OUT, MODE == 0>), g, dim3(64), lds, st, A, sa, W, sw, Y, m, n, k); break;
+    }
+    return hipGetLastError();
+  }
   switch (sk) {
     case 8: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 8, PF, OUT>), g, dim3(512), 0, st, A, sa, W, sw, Y, m, n, k); break;
     case 4: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 4, PF, OUT>), g, dim3(256), 0, st, A, sa, W, sw, Y, m, n, k); break;
@@ -974,11 +1030,6 @@ inline int pick_ring_depth(int64_t N, int nwv) {
   const int64_t waves_per_cu = nwv * ((wgs + kCUs - 1) / kCUs);
   return waves_per_cu <= 4 ? 8 : (waves_per_cu <= 8 ? 4 : 2);
 }
-
-// Dynamic LDS of the block-wise shared-activation kernel: 16 MF rows of
-// activation scales, KB | 1 floats apart.
-inline size_t shared_scale_lds(int MF, int64_t K) { return (size_t)16 * MF * ((K >> 7) | 1) * 4; }
-constexpr size_t kSharedScaleLdsMax = 64 * 1024;
 
 template <int MODE, int MF, int NWV, int PF, int OUT>
 hipError_t shared_launch(const int8_t* A, const float* sa, const int8_t* W, const float* sw, void* Y, int64_t M,
