@@ -1003,8 +1003,10 @@ hipError_t decode_launch(const int8_t* A, const float* sa, const int8_t* W, cons
   const dim3 g((unsigned)wgs);
   const int m = (int)M, n = (int)N, k = (int)K;
   // block-wise: activation scales staged in LDS where they fit the budget
+  // (64-row tiles only with eight waves, whose launch bounds hold the kernel
+  // to 208 registers; with fewer it takes 260 and one wave per SIMD)
   const size_t lds = shared_scale_lds(MF, K);
-  if (MODE == 0 && lds <= kSharedScaleLdsMax) {
+  if (MODE == 0 && lds <= kSharedScaleLdsMax && (MF < 4 || sk == 8)) {
     switch (sk) {
       case 8: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 8, PF, OUT, MODE == 0>), g, dim3(512), lds, st, A, sa, W, sw, Y, m, n, k); break;
       case 4: hipLaunchKernelGGL((k_decode_w8a8<MODE, MF, FNW, 4, PF, OUT, MODE == 0>), g, dim3(256), lds, st, A, sa, W, sw, Y, m, n, k); break;
